@@ -1,0 +1,38 @@
+// Host-side launchers of the kernels (one translation unit per kernel family).
+// Every launcher assumes its shape has been validated by the C-ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "mla.h"
+
+namespace mla {
+
+hipError_t launch_absorb_q(const mla_shape_t& s, const void* q, const void* w_uk,
+                           void* q_abs, hipStream_t st);
+hipError_t launch_decode_absorbed_generic(const mla_shape_t& s, const void* q_abs,
+                                          const void* pool, const int32_t* pt,
+                                          const int32_t* lens, float* o_part,
+                                          float* lse_part, hipStream_t st);
+hipError_t launch_decode_absorbed_mfma(const mla_shape_t& s, const void* q_abs,
+                                       const void* pool, const int32_t* pt,
+                                       const int32_t* lens, float* o_part, float* lse_part,
+                                       hipStream_t st);
+bool decode_absorbed_mfma_supported(const mla_shape_t& s);
+hipError_t launch_combine(const mla_shape_t& s, int width, const float* o_part,
+                          const float* lse_part, float* o, float* lse, hipStream_t st);
+hipError_t launch_out_uv(const mla_shape_t& s, const float* o_lat, const void* w_uv,
+                         float* out, hipStream_t st);
+hipError_t launch_gqa_decode_generic(const mla_shape_t& s, const void* q, const void* k,
+                                     const void* v, const void* kr, const int32_t* pt,
+                                     const int32_t* lens, float* o_part, float* lse_part,
+                                     hipStream_t st);
+hipError_t launch_gqa_decode_mfma(const mla_shape_t& s, const void* q, const void* k,
+                                  const void* v, const void* kr, const int32_t* pt,
+                                  const int32_t* lens, float* o_part, float* lse_part,
+                                  hipStream_t st);
+bool gqa_decode_mfma_supported(const mla_shape_t& s);
+hipError_t launch_expand_cache(const mla_shape_t& s, const void* pool, const void* w_uk,
+                               const void* w_uv, void* k, void* v, void* kr,
+                               hipStream_t st);
+
+}  // namespace mla

@@ -1,0 +1,183 @@
+/*
+ * mla.h - C ABI of libmla: single-step MLA / GQLA decode attention on gfx950.
+ *
+ * Method (pages named by title and section):
+ *  - "MLA and GRPO architecture", section 2, "The Mathematics of MLA": every token's
+ *    keys and values come from one cached latent c_t through per-head up-projections
+ *    k_t = W_UK c_t, v_t = W_UV c_t; "Decoupled Rotary Position Embeddings": a separate
+ *    RoPE key k^R_t is cached beside c_t, so a cache row is [c_t ; k^R_t].
+ *  - "How to upgrade GQA models to MLA...", "Under the hood", Decompression Multiplex:
+ *    by associativity W_UK moves onto the query, so decode scores the query against
+ *    the latent directly and the keys are never decompressed (the absorbed form).
+ *  - "GQLA: Group-Query Latent Attention..." (abstract) and the AI Radio episode on it
+ *    ("The paper's summary"): with up-projections shared by groups of query heads the
+ *    same weights also allow a GQA path over a per-group expanded cache (per-group K and
+ *    V plus the shared RoPE key); both paths give the same attention.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor arguments are DEVICE pointers owned by the caller; the library allocates
+ *    nothing, keeps no global state and never synchronises.  Every call is asynchronous
+ *    on `stream` (0 = the null stream).  Tensors are dense, row-major, in the layouts
+ *    given below; `dtype` (MLA_F32 or MLA_BF16) is the element type of q, q_abs, the
+ *    caches and the weights.  Split partials, latent outputs and final outputs are fp32.
+ *  - Query head h uses weight head w(h) = h / (n_heads / n_wheads): n_wheads = n_heads
+ *    is MLA, n_wheads = G < n_heads is GQLA with contiguous groups.
+ *  - ctx_lens[b] = T_b counts every cached token of sequence b INCLUDING its s_q new
+ *    ones; query row s (0 <= s < s_q) attends to tokens 0 .. T_b - s_q + s (causal
+ *    within the new tokens).  ctx_lens and page_table are device data and must satisfy
+ *    0 <= T_b <= max_pages * page_size and 0 <= page_table[b][i] < num_pages for
+ *    i < ceil(T_b / page_size); entries past that are never read (use -1).  These
+ *    device values are not validated: breaking them is undefined behaviour.
+ *  - Split-KV: sequence b is cut into n_splits chunks.  split_tokens == 0: chunk length
+ *    L_b = ceil(ceil(T_b / n_splits) / page_size) * page_size; split_tokens > 0: fixed
+ *    L = split_tokens (a multiple of page_size, and n_splits * L must cover
+ *    max_pages * page_size).  Chunk u covers tokens [u*L, min((u+1)*L, T_b)).  A chunk
+ *    with no visible token yields o = 0 and lse = -inf.
+ *  - Errors: arguments are validated on the host before any HIP call; a failing check
+ *    returns its status and launches nothing.  A launch failure returns MLA_ERR_HIP.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,        /* a required pointer is NULL                                 */
+  MLA_ERR_SHAPE = 2,       /* a size is non-positive or inconsistent                     */
+  MLA_ERR_UNSUPPORTED = 3, /* valid but not implemented (dims, dtype, page size)         */
+  MLA_ERR_HIP = 4          /* a HIP launch or runtime call failed                        */
+} mla_status_t;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
+
+typedef struct {
+  int32_t batch;         /* B                                                          */
+  int32_t s_q;           /* new query tokens per sequence (1, or 2 for MTP decode)     */
+  int32_t n_heads;       /* query heads H                                              */
+  int32_t n_wheads;      /* weight heads: H for MLA, G groups for GQLA; H % n_wheads == 0 */
+  int32_t d_c;           /* latent width (512)                                         */
+  int32_t d_rope;        /* decoupled RoPE key width (64)                              */
+  int32_t d_nope;        /* no-position query/key head width (128)                     */
+  int32_t d_v;           /* value head width (128)                                     */
+  int32_t page_size;     /* tokens per cache page; must be 64                          */
+  int32_t max_pages;     /* row stride of page_table                                   */
+  int32_t num_pages;     /* pages in each pool                                         */
+  int32_t n_splits;      /* S >= 1 split-KV chunks per sequence                         */
+  int32_t split_tokens;  /* 0 = even page-aligned chunks, >0 = fixed chunk length      */
+  float softmax_scale;   /* sigma applied to q.k                                      */
+  mla_dtype_t dtype;     /* element type of q, q_abs, caches and weights               */
+} mla_shape_t;
+
+/* Supported dimensions: d_c, d_rope, d_nope, d_v multiples of 8 with d_c <= 1024,
+ * d_c + d_rope <= 1024, d_nope + d_rope <= 1024, d_v <= 1024; page_size == 64.  The
+ * bf16 shape d_c = 512, d_rope = 64 runs on the matrix-core kernels, others on the
+ * generic kernels (same results up to rounding order). */
+
+/* a1 - query absorption.
+ * q_abs[b,s,h, 0:d_c]      = sum_i q[b,s,h,i] * w_uk[w(h), i, :]      (i < d_nope)
+ * q_abs[b,s,h, d_c:d_c+dR] = q[b,s,h, d_nope : d_nope+d_rope]           (RoPE part copied)
+ * q     [B, s_q, H, d_nope + d_rope]   dtype; RoPE part already rotated
+ * w_uk  [n_wheads, d_nope, d_c]        dtype
+ * q_abs [B, s_q, H, d_c + d_rope]      dtype (fp32 accumulate, one rounding to dtype)
+ * Page: "How to upgrade GQA models to MLA...", Under the hood (Decompression Multiplex). */
+mla_status_t mla_absorb_q(const mla_shape_t* shape, const void* q, const void* w_uk,
+                          void* q_abs, hipStream_t stream);
+
+/* a2 - absorbed decode over the paged latent cache, split-KV with online softmax.
+ * For every (b, s, h) and chunk u, over the visible tokens t of u:
+ *   z_t = softmax_scale * <q_abs[b,s,h], R_b[t]>,  R_b[t] = kv_pool[page_table[b][t/P], t%P]
+ *   o_part[b,s,h,u,:] = sum_t softmax_u(z)_t * R_b[t][0:d_c],  lse_part = log sum_t e^{z_t}
+ * q_abs      [B, s_q, H, D]        dtype, D = d_c + d_rope
+ * kv_pool    [num_pages, P, D]     dtype; row = [c_t ; k^R_t]
+ * page_table [B, max_pages]        int32;  ctx_lens [B] int32
+ * o_part     [B, s_q, H, S, d_c]   fp32;   lse_part [B, s_q, H, S] fp32
+ * Pages: "MLA and GRPO architecture" s.2 (cached state, decompression); GQLA abstract
+ * and AI Radio "Key concepts" (the latent serves as shared key and value). */
+mla_status_t mla_decode_absorbed(const mla_shape_t* shape, const void* q_abs,
+                                 const void* kv_pool, const int32_t* page_table,
+                                 const int32_t* ctx_lens, float* o_part, float* lse_part,
+                                 hipStream_t stream);
+
+/* a3 - merge split partials: lse = log sum_u e^{lse_u}, o = sum_u e^{lse_u - lse} o_u.
+ * o_part [B, s_q, H, S, width] fp32, lse_part [B, s_q, H, S] fp32 ->
+ * o [B, s_q, H, width] fp32, lse [B, s_q, H] fp32 (lse may be NULL).
+ * width = d_c after mla_decode_absorbed, d_v after gqla_decode_gqa.  Rows whose chunks
+ * are all empty give o = 0, lse = -inf.  (Log-sum-exp identity of softmax over disjoint
+ * token sets; the chunking itself is not on the pages.) */
+mla_status_t mla_splitkv_combine(const mla_shape_t* shape, int32_t width,
+                                 const float* o_part, const float* lse_part, float* o,
+                                 float* lse, hipStream_t stream);
+
+/* a4 - value up-projection after the latent reduction.
+ * out[b,s,h,:] = w_uv[w(h)] @ o_lat[b,s,h,:]
+ * o_lat [B, s_q, H, d_c] fp32;  w_uv [n_wheads, d_v, d_c] dtype;  out [B, s_q, H, d_v] fp32
+ * Page: "MLA and GRPO architecture" s.2 "The Mathematics of MLA" (v = W_UV c), moved
+ * after the reduction by associativity. */
+mla_status_t mla_out_uv(const mla_shape_t* shape, const float* o_lat, const void* w_uv,
+                        float* out, hipStream_t stream);
+
+/* a5 - GQLA GQA path over the per-group expanded cache, split-KV with online softmax.
+ * Head h in group j = w(h):  z_t = softmax_scale * (<q_nope, K[t,j]> + <q_rope, kR[t]>),
+ *   o_part[b,s,h,u,:] = sum_t softmax_u(z)_t V[t,j],  lse_part as in a2.
+ * q       [B, s_q, H, d_nope + d_rope]     dtype
+ * k_pool  [num_pages, P, G, d_nope]        dtype  (G = n_wheads)
+ * v_pool  [num_pages, P, G, d_v]           dtype
+ * kr_pool [num_pages, P, d_rope]           dtype
+ * o_part  [B, s_q, H, S, d_v] fp32;  lse_part [B, s_q, H, S] fp32
+ * Pages: GQLA abstract; AI Radio "The paper's summary" (per-group K, V and shared RoPE key). */
+mla_status_t gqla_decode_gqa(const mla_shape_t* shape, const void* q, const void* k_pool,
+                             const void* v_pool, const void* kr_pool,
+                             const int32_t* page_table, const int32_t* ctx_lens,
+                             float* o_part, float* lse_part, hipStream_t stream);
+
+/* a6 - build the GQA path's per-group cache from the latent cache (set-up, not per step).
+ * For every pool row [c ; k^R]: k_pool[p,r,j] = w_uk[j] @ c, v_pool[p,r,j] = w_uv[j] @ c,
+ * kr_pool[p,r] = k^R; fp32 accumulate, rounded once to dtype.  Every row of the pool is
+ * converted, padding rows included.  Shapes as in a5 / a1 / a4.  Page: AI Radio episode
+ * on GQLA, "The paper's summary". */
+mla_status_t gqla_expand_cache(const mla_shape_t* shape, const void* kv_pool,
+                               const void* w_uk, const void* w_uv, void* k_pool,
+                               void* v_pool, void* kr_pool, hipStream_t stream);
+
+/* Whole absorbed step a1 -> a2 -> a3 -> a4 on one stream.  The caller provides the
+ * workspaces: q_abs [B,s_q,H,D] dtype, o_part [B,s_q,H,S,d_c] fp32,
+ * lse_part [B,s_q,H,S] fp32, o_lat [B,s_q,H,d_c] fp32.  out [B,s_q,H,d_v] fp32,
+ * lse [B,s_q,H] fp32 (may be NULL). */
+mla_status_t mla_decode_step(const mla_shape_t* shape, const void* q, const void* w_uk,
+                             const void* w_uv, const void* kv_pool,
+                             const int32_t* page_table, const int32_t* ctx_lens,
+                             void* q_abs, float* o_part, float* lse_part, float* o_lat,
+                             float* out, float* lse, hipStream_t stream);
+
+/* Whole GQA-path step a5 -> a3 on one stream: o_part [B,s_q,H,S,d_v] and lse_part are
+ * caller workspaces; out [B,s_q,H,d_v] fp32, lse [B,s_q,H] fp32 (may be NULL). */
+mla_status_t gqla_decode_step(const mla_shape_t* shape, const void* q, const void* k_pool,
+                              const void* v_pool, const void* kr_pool,
+                              const int32_t* page_table, const int32_t* ctx_lens,
+                              float* o_part, float* lse_part, float* out, float* lse,
+                              hipStream_t stream);
+
+/* Cache scalars per token and layer.  MQA-absorb / MLA: d_c + d_rope ("MLA and GRPO
+ * architecture", Decoupled RoPE).  GQA path: G * (d_nope + d_v) + d_rope (AI Radio, "The
+ * paper's summary").  Return -1 for a NULL or invalid shape. */
+int64_t mla_cache_scalars_per_token(const mla_shape_t* shape);
+int64_t gqla_cache_scalars_per_token(const mla_shape_t* shape);
+
+/* Which kernel family a2 / a5 would run for this shape: 1 = matrix-core (MFMA) kernel,
+ * 0 = generic kernel, -1 = invalid or unsupported shape.  Host-only, no HIP call. */
+int32_t mla_decode_kernel_kind(const mla_shape_t* shape);
+int32_t gqla_decode_kernel_kind(const mla_shape_t* shape);
+
+/* Static description of a status code (never NULL). */
+const char* mla_status_str(mla_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H */

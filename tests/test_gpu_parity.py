@@ -1,0 +1,289 @@
+"""GPU parity: every C-ABI entry point against the float64 CPU oracle (needs gfx950).
+
+Error measure (as the tolerances are stated): rel_err = max |gpu - oracle| / max |oracle|
+over the compared tensor.  Bars: 1e-4 for fp32 workloads, 2e-2 for bf16 cache / fp32
+accumulate workloads.  Small cases compare every output; full-size workloads compare
+sampled (sequence, head) rows that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import head_latent_attention_02_amd as mla
+from oracle import mla as ref
+from workloads import Config, get_config, make_inputs
+from workloads.device import DeviceInputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def rel_err(got, want):
+    got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
+    assert got.shape == want.shape
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isneginf(got), np.isneginf(want)), "-inf pattern differs"
+    assert np.all(np.isfinite(got[fin])), "non-finite values where the oracle is finite"
+    return float(np.max(np.abs(got[fin] - want[fin])) / np.max(np.abs(want[fin])))
+
+
+def announce(msg):
+    print(msg, flush=True)
+
+
+def absorbed_step(d, sync=True):
+    c = d.inp.cfg
+    op = d.o_part_view(c.d_c)
+    mla.mla_absorb_q(d.shape, d.q, d.w_uk, d.q_abs)
+    mla.mla_decode_absorbed(d.shape, d.q_abs, d.pool, d.page_table, d.ctx_lens, op,
+                            d.lse_part)
+    mla.mla_splitkv_combine(d.shape, c.d_c, op, d.lse_part, d.o_lat, d.lse)
+    mla.mla_out_uv(d.shape, d.o_lat, d.w_uv, d.out)
+    if sync:
+        torch.cuda.synchronize()
+    return op
+
+
+def small(name="dsv2-b16-t4096", **kw):
+    return get_config(name, **kw)
+
+
+def check_absorbed_all_steps(inp, S=None, split_tokens=None):
+    """Compare a1..a4 one by one against the oracle's plain steps; returns the errors."""
+    c = inp.cfg
+    announce(f"case {c.name} B={c.batch} s_q={c.s_q} H={c.n_heads}/{c.n_wheads} "
+             f"ctx={list(inp.ctx_lens)[:6]} S={S or c.n_splits} L={split_tokens}")
+    d = DeviceInputs(inp, n_splits=S, split_tokens=split_tokens)
+    op = absorbed_step(d)
+    tol = TOL[c.dtype]
+    sh = d.shape
+    pool = inp.pool_view()
+    q_abs = ref.absorb_query(inp.q, inp.w_uk, c.d_nope)
+    e1 = rel_err(d.q_abs.float().cpu().numpy(), q_abs)
+    o_p, l_p = ref.absorbed_split_partials(q_abs, pool, inp.page_table, inp.ctx_lens,
+                                           sh.n_splits, c.scale, c.page_size, c.d_c,
+                                           sh.split_tokens)
+    e2 = rel_err(op.cpu().numpy(), o_p)
+    e2l = rel_err(d.lse_part.cpu().numpy(), l_p)
+    o_l, lse = ref.combine_splits(o_p, l_p)
+    e3 = rel_err(d.o_lat.cpu().numpy(), o_l)
+    out, lse_n = ref.mla_decode_naive(inp.q, pool, inp.page_table, inp.ctx_lens, inp.w_uk,
+                                      inp.w_uv, c.scale, c.page_size, c.d_c)
+    e4 = rel_err(d.out.cpu().numpy(), out)
+    e4l = rel_err(d.lse.cpu().numpy(), lse_n)
+    errs = dict(absorb=e1, partial_o=e2, partial_lse=e2l, combine=e3, out=e4, lse=e4l)
+    announce(f"  errors {errs} kind={mla.mla_decode_kernel_kind(sh)}")
+    for k, v in errs.items():
+        assert v <= tol, f"{k}: {v} > {tol}"
+    return errs
+
+
+# ------------------------------------------------------------------ tiny fp32
+
+@pytest.mark.parametrize("S,L", [(1, 0), (4, 0), (2, 128), (7, 0)])
+def test_tiny_f32_all_steps(S, L):
+    inp = make_inputs(get_config("tiny-f32"))
+    check_absorbed_all_steps(inp, S=S, split_tokens=L)
+
+
+def test_tiny_f32_ragged_mtp_and_empty_rows():
+    cfg = get_config("tiny-f32", batch=4, s_q=2, ctx=("list", [1, 2, 65, 255]))
+    check_absorbed_all_steps(make_inputs(cfg, seed=1), S=5)
+
+
+def test_tiny_f32_step_entry_point_matches_steps():
+    inp = make_inputs(get_config("tiny-f32"))
+    d = DeviceInputs(inp)
+    absorbed_step(d)
+    out1, lse1 = d.out.clone(), d.lse.clone()
+    d.out.fill_(7.0)
+    mla.mla_decode_step(d.shape, d.q, d.w_uk, d.w_uv, d.pool, d.page_table, d.ctx_lens,
+                        d.q_abs, d.o_part, d.lse_part, d.o_lat, d.out, d.lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, d.out) and torch.equal(lse1, d.lse)
+
+
+# ------------------------------------------------------------- bf16, small sizes
+
+@pytest.mark.parametrize("S,L,ctx", [
+    (1, 0, [1000, 64]), (4, 0, [4096, 577]), (3, 128, [300, 129]), (8, 0, [33, 1])])
+def test_bf16_mla_small_all_steps(S, L, ctx):
+    cfg = small(batch=len(ctx), ctx=("list", ctx))
+    check_absorbed_all_steps(make_inputs(cfg, seed=2), S=S, split_tokens=L)
+
+
+@pytest.mark.parametrize("ctx", [[2, 3, 130, 1025], [64, 65, 127, 2000]])
+def test_bf16_mtp_small_all_steps(ctx):
+    cfg = small(batch=len(ctx), s_q=2, ctx=("list", ctx))
+    check_absorbed_all_steps(make_inputs(cfg, seed=3), S=3)
+
+
+def test_bf16_gqla_absorbed_small():
+    cfg = get_config("gqla-b32-t8192", batch=3, ctx=("list", [500, 64, 1999]))
+    check_absorbed_all_steps(make_inputs(cfg, seed=4), S=2)
+
+
+def test_identity_vs_permuted_page_table_bitwise():
+    cfg = small(batch=3, ctx=("list", [700, 300, 1100]))
+    a = make_inputs(cfg, seed=5)
+    d = DeviceInputs(a)
+    absorbed_step(d)
+    out_perm = d.out.clone()
+    # the same logical content laid out in order
+    order = [int(p) for b in range(cfg.batch) for p in a.page_table[b] if p >= 0]
+    b_in = make_inputs(cfg, seed=5)
+    b_in.pool = a.pool[order]
+    tbl = np.full_like(a.page_table, -1)
+    off = 0
+    for b in range(cfg.batch):
+        n = int(np.sum(a.page_table[b] >= 0))
+        tbl[b, :n] = np.arange(off, off + n)
+        off += n
+    b_in.page_table = tbl
+    d2 = DeviceInputs(b_in)
+    absorbed_step(d2)
+    assert torch.equal(out_perm, d2.out)
+
+
+def test_deterministic_over_repeats():
+    cfg = small(batch=2, ctx=("list", [1500, 900]))
+    d = DeviceInputs(make_inputs(cfg, seed=6))
+    absorbed_step(d)
+    first = d.out.clone()
+    for _ in range(5):
+        absorbed_step(d)
+        assert torch.equal(first, d.out)
+
+
+def test_negative_control_uniform_attention_fails():
+    """Uniform attention (q = 0) is far from the real output: the bar has teeth."""
+    cfg = small(batch=2, ctx=("list", [1024, 512]))
+    inp = make_inputs(cfg, seed=7)
+    out, _ = ref.mla_decode_naive(inp.q, inp.pool_view(), inp.page_table, inp.ctx_lens,
+                                  inp.w_uk, inp.w_uv, cfg.scale, cfg.page_size, cfg.d_c,
+                                  heads=[0, 5, 64])
+    inp.q = np.zeros_like(inp.q)
+    d = DeviceInputs(inp)
+    absorbed_step(d)
+    err = rel_err(d.out.cpu().numpy()[:, :, [0, 5, 64]], out[:, :, [0, 5, 64]])
+    announce(f"  negative control rel err {err:.3f}")
+    assert err > 10 * TOL["bf16"]
+
+
+def test_nan_poisoned_pages_never_read():
+    cfg = small(batch=2, ctx=("list", [100, 65]))
+    inp = make_inputs(cfg, seed=8, extra_pages=3, max_pages=6)
+    d = DeviceInputs(inp)
+    absorbed_step(d)
+    assert torch.isfinite(d.out).all() and torch.isfinite(d.o_lat).all()
+
+
+# ----------------------------------------------------------------- GQA path
+
+def gqa_step(d, k, v, kr, sync=True):
+    c = d.inp.cfg
+    op = d.o_part_view(c.d_v)
+    mla.gqla_decode_gqa(d.shape, d.q, k, v, kr, d.page_table, d.ctx_lens, op, d.lse_part)
+    mla.mla_splitkv_combine(d.shape, c.d_v, op, d.lse_part, d.out, d.lse)
+    if sync:
+        torch.cuda.synchronize()
+    return op
+
+
+def expanded_pools(d):
+    c = d.inp.cfg
+    wdt = torch.bfloat16 if d.inp.is_bf16 else torch.float32
+    n = d.inp.num_pages
+    k = torch.empty(n, c.page_size, c.n_wheads, c.d_nope, dtype=wdt, device="cuda")
+    v = torch.empty(n, c.page_size, c.n_wheads, c.d_v, dtype=wdt, device="cuda")
+    kr = torch.empty(n, c.page_size, c.d_rope, dtype=wdt, device="cuda")
+    return k, v, kr
+
+
+@pytest.mark.parametrize("dtype,ctx,S", [("f32", [300, 64, 1], 3), ("bf16", [1000, 129], 2),
+                                         ("bf16", [4096, 2000], 4)])
+def test_gqla_expand_and_gqa_path(dtype, ctx, S):
+    if dtype == "f32":
+        cfg = Config("gqla-tiny-f32", "f32", len(ctx), 1, 8, 2, 64, 16, 32, 32,
+                     ("list", ctx), S)
+    else:
+        cfg = get_config("gqla-b32-t8192", batch=len(ctx), ctx=("list", ctx), n_splits=S)
+    inp = make_inputs(cfg, seed=9)
+    announce(f"case gqa {dtype} ctx={ctx} S={S}")
+    d = DeviceInputs(inp)
+    k, v, kr = expanded_pools(d)
+    mla.gqla_expand_cache(d.shape, d.pool, d.w_uk, d.w_uv, k, v, kr)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    # a6 against the oracle's expansion (rows past the context are NaN on both sides)
+    ek, ev, ekr = ref.expand_cache(inp.pool_f32(), inp.w_uk, inp.w_uv, cfg.d_c)
+    fin = np.isfinite(ek)
+    gk = k.float().cpu().numpy()
+    assert np.array_equal(np.isfinite(gk), fin)
+    assert rel_err(gk[fin], ek[fin]) <= tol
+    gv = v.float().cpu().numpy()
+    assert rel_err(gv[np.isfinite(ev)], ev[np.isfinite(ev)]) <= tol
+    assert np.array_equal(kr.float().cpu().numpy(), ekr.astype(np.float32), equal_nan=True)
+    # a5 + a3 against the plain definition (naive over the latent cache)
+    gqa_step(d, k, v, kr)
+    out, lse = ref.mla_decode_naive(inp.q, inp.pool_view(), inp.page_table, inp.ctx_lens,
+                                    inp.w_uk, inp.w_uv, cfg.scale, cfg.page_size, cfg.d_c)
+    e_out = rel_err(d.out.cpu().numpy(), out)
+    e_lse = rel_err(d.lse.cpu().numpy(), lse)
+    announce(f"  gqa errors out={e_out:.3e} lse={e_lse:.3e} "
+             f"kind={mla.gqla_decode_kernel_kind(d.shape)}")
+    assert e_out <= tol and e_lse <= tol
+
+
+def test_gqa_decode_on_oracle_expanded_cache():
+    """a5 alone: fed the oracle's expansion rounded to bf16, compared with the oracle's
+    GQA-path partials over that same cache."""
+    from workloads.gen import bf16_round
+    cfg = get_config("gqla-b32-t8192", batch=2, s_q=2, ctx=("list", [777, 130]), n_splits=3)
+    inp = make_inputs(cfg, seed=10)
+    ek, ev, ekr = ref.expand_cache(inp.pool_f32(), inp.w_uk, inp.w_uv, cfg.d_c)
+    k_np, v_np, kr_np = (bf16_round(x.astype(np.float32)) for x in (ek, ev, ekr))
+    d = DeviceInputs(inp)
+    k = torch.from_numpy(k_np).cuda().to(torch.bfloat16)
+    v = torch.from_numpy(v_np).cuda().to(torch.bfloat16)
+    kr = torch.from_numpy(kr_np).cuda().to(torch.bfloat16)
+    op = gqa_step(d, k, v, kr)
+    o_p, l_p = ref.gqa_split_partials(inp.q, k_np, v_np, kr_np, inp.page_table, inp.ctx_lens,
+                                      3, cfg.scale, cfg.page_size)
+    assert rel_err(op.cpu().numpy(), o_p) <= TOL["bf16"]
+    assert rel_err(d.lse_part.cpu().numpy(), l_p) <= TOL["bf16"]
+
+
+# -------------------------------------------------- full-size workloads (sampled)
+
+def sampled_full_check(cfg, batches, heads, S=None, split_tokens=None):
+    inp = make_inputs(cfg)
+    announce(f"case full {cfg.name} tokens={inp.total_tokens} S={S or cfg.n_splits}")
+    d = DeviceInputs(inp, n_splits=S, split_tokens=split_tokens)
+    absorbed_step(d)
+    got = d.out.cpu().numpy()
+    got_lse = d.lse.cpu().numpy()
+    del d
+    torch.cuda.empty_cache()
+    want, lse = ref.mla_decode_naive(inp.q, inp.pool_view(), inp.page_table, inp.ctx_lens,
+                                     inp.w_uk, inp.w_uv, cfg.scale, cfg.page_size, cfg.d_c,
+                                     batches=batches, heads=heads)
+    sel = np.ix_(batches, range(cfg.s_q), heads)
+    e = rel_err(got[sel], want[sel])
+    el = rel_err(got_lse[sel], lse[sel])
+    announce(f"  sampled errors out={e:.3e} lse={el:.3e} "
+             f"(rows {len(batches)}x{cfg.s_q}x{len(heads)})")
+    assert e <= TOL[cfg.dtype] and el <= TOL[cfg.dtype]
+
+
+def test_full_dsv2_b16_t4096():
+    sampled_full_check(get_config("dsv2-b16-t4096"), list(range(16)), [0, 31, 64, 127])
+
+
+def test_full_long_b4_t131072():
+    sampled_full_check(get_config("long-b4-t131072"), [0, 1, 2, 3], [0, 127, 45, 90])
+
+
+def test_full_mtp_b64_ragged():
+    sampled_full_check(get_config("mtp-b64-ragged"), [0, 17, 40, 63], [0, 127, 77])
