@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Throughput of single-step absorbed MLA decode on one MI355X.
+
+One step = the whole absorbed path on one batch: query absorption -> split-KV decode
+over the paged latent cache -> split combine -> value up-projection, all through the C
+ABI of libmla.so on one HIP stream.  The workload (default: batch 4 x 131072-token
+contexts, 128 heads, latent 512 + RoPE 64, bf16, split-KV over 32 chunks) is seeded and
+synthetic and is resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is cached-latent-tokens/s of the whole step.
+`roofline` describes the decode kernel (the dominant one): algorithmic bytes (every
+cached token's 576 bf16 once) / its average launch time, measured with HIP events on
+the launch stream; `traffic` comes from the committed rocprofv3 counter summary when it
+was taken on the current kernel source, else null.  `cpu_baseline` times the float64
+CPU oracle (naive, non-absorbed MLA) on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
+KERNEL_SRC = os.path.join(ROOT, "head_latent_attention_02_amd", "csrc", "decode_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_absorbed_long_b4_t131072_traffic.json")
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long-b4-t131072")
+    ap.add_argument("--splits", type=int, default=None, help="override n_splits")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time the other workloads (stderr lines)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28   # 1 GiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n}))
+
+
+def cpu_baseline(inp, seconds):
+    """Time the oracle on whole (sequence, head) rows of the workload until ~seconds."""
+    import numpy as np
+    from oracle import mla as ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    c = inp.cfg
+    pool = inp.pool_view()
+    done, t0 = 0, time.perf_counter()
+    h = 0
+    while True:
+        ref.mla_decode_naive(inp.q, pool, inp.page_table, inp.ctx_lens, inp.w_uk, inp.w_uv,
+                             c.scale, c.page_size, c.d_c, batches=[0], heads=[h])
+        done += 1
+        h = (h + 1) % c.n_heads
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    per_row = el / done                     # one (sequence, head) row over T_0 tokens
+    step_s = per_row * c.batch * c.n_heads * float(np.mean(inp.ctx_lens)) / float(inp.ctx_lens[0])
+    return {"value": inp.total_tokens / step_s, "unit": "cached-latent-tokens/s",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} (sequence 0, head) rows of {int(inp.ctx_lens[0])} tokens in "
+                      f"{el:.1f} s, scaled to all {c.batch}x{c.n_heads} rows"}
+
+
+def time_workload(name, steps, warmup, splits=None):
+    import numpy as np
+    import torch
+    import head_latent_attention_02_amd as mla
+    from workloads import get_config, make_inputs
+    from workloads.device import DeviceInputs
+
+    cfg = get_config(name)
+    if splits:
+        cfg = cfg.with_(n_splits=splits)
+    inp = make_inputs(cfg)
+    d = DeviceInputs(inp)
+    sh = d.shape
+    op = d.o_part_view(cfg.d_c)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(ev=None):
+        mla.mla_absorb_q(sh, d.q, d.w_uk, d.q_abs, stream=sp)
+        if ev:
+            ev[0].record(stream)
+        mla.mla_decode_absorbed(sh, d.q_abs, d.pool, d.page_table, d.ctx_lens, op,
+                                d.lse_part, stream=sp)
+        if ev:
+            ev[1].record(stream)
+        mla.mla_splitkv_combine(sh, cfg.d_c, op, d.lse_part, d.o_lat, d.lse, stream=sp)
+        mla.mla_out_uv(sh, d.o_lat, d.w_uv, d.out, stream=sp)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return inp, d, wall / steps * 1e3, dec_ms
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the "
+              "decode path has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import head_latent_attention_02_amd as mla
+
+    inp, d, ms_step, dec_ms = time_workload(args.workload, args.steps, args.warmup, args.splits)
+    c = inp.cfg
+    tokens = inp.total_tokens
+    dec_bytes = tokens * c.D * 2                                  # algorithmic cache bytes
+    dec_flops = tokens * c.s_q * c.n_heads * (2 * c.D + 2 * c.d_c)
+    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_sha") == kernel_hash() and tr.get("workload") == args.workload:
+            traffic = tr.get("hbm_bytes_per_launch")
+    line = {
+        "metric": "MLA decode cached-latent-tokens/s; % HBM-BW and % bf16 MFMA peak, 1 GPU",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "cached-latent-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) latents, permuted page table)",
+        "config": {"workload": args.workload, "batch": c.batch, "ctx": int(inp.ctx_lens[0]),
+                   "s_q": c.s_q, "heads": c.n_heads, "d_c": c.d_c, "d_rope": c.d_rope,
+                   "n_splits": d.shape.n_splits, "page_size": c.page_size,
+                   "path": "absorbed", "kernel": "mfma" if mla.mla_decode_kernel_kind(d.shape)
+                   == 1 else "generic"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "mla_decode_absorbed", "kernel_ms": dec_ms,
+                     "mfma_tflops": dec_flops / (dec_ms * 1e-3) / 1e12,
+                     "mfma_frac": dec_flops / (dec_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    if args.extra:
+        del d
+        for name in ("dsv2-b16-t4096", "mtp-b64-ragged", "gqla-b32-t65536"):
+            i2, d2, ms2, dms2 = time_workload(name, args.steps, args.warmup)
+            b2 = i2.total_tokens * i2.cfg.D * 2
+            print(json.dumps({"workload": name, "ms_per_step": ms2, "decode_ms": dms2,
+                              "tokens_per_s": i2.total_tokens / (ms2 * 1e-3),
+                              "decode_GBs": b2 / (dms2 * 1e-3) / 1e9}), file=sys.stderr,
+                  flush=True)
+            del d2
+
+
+if __name__ == "__main__":
+    main()

@@ -1,12 +1,747 @@
-// Matrix-core (MFMA) absorbed decode: not built yet; every shape takes the generic path.
+// Matrix-core (MFMA) absorbed decode for bf16 latent caches with d_c = 512, d_rope = 64.
+//
+// What it computes is the split-KV form of absorbed MLA attention: per chunk u and
+// query row (s, h), softmax over the chunk's visible tokens of
+// z_t = sigma <q_abs, [c_t ; k^R_t]>, reducing over the latent c_t itself
+// ("MLA and GRPO architecture", s.2: the cached state is [c_t, k^R_t];
+// "How to upgrade GQA models to MLA...", Under the hood: with W_UK folded onto the
+// query the keys are never decompressed; AI Radio episode on GQLA, "Key concepts": on
+// the MQA-absorb path the latent is the shared key and value).
+//
+// Work decomposition (one workgroup = one sequence b, one chunk u, ROWS = 32*NQ query
+// rows, rows being the flattened (s, h) pairs):
+//  * NQ "score" waves each own 32 query rows.  Their q_abs rows stay in registers as the
+//    B operand of v_mfma_f32_32x32x16_bf16.  Per 32-token tile they load the 32 cache
+//    rows (576 bf16 each) from HBM straight into A-operand registers, 16 bytes per lane
+//    and K-step, and compute S^T[token][row] over the 576-wide contraction.  The loads of
+//    tile k+1 are issued into each register right after its MFMA has consumed it, so a
+//    whole tile of loads is always in flight.  Each score wave also writes its share of
+//    the tile's 512 latent columns to LDS for the value product.
+//  * The same score waves run the online softmax in the log2 domain with a lazy
+//    reference: the per-row reference maximum only moves when a score exceeds it by more
+//    than a slack of 32 (P then stays below 2^32, far inside bf16/fp32 range; numerator
+//    and denominator share the reference, so the result is exact).  They publish P (bf16)
+//    and a per-row factor (1 unless the reference moved) through LDS.
+//  * NQ "value" waves each own 512/NQ latent columns of O^T for all ROWS rows
+//    (accumulators in AGPRs).  They read the latent tile transposed with
+//    ds_read_b64_tr_b16 as the A operand and P^T as the B operand.  When a reference
+//    moved (rare), they fold their accumulators, rescaled, into the workgroup's own
+//    o_part slot and restart from zero; the epilogue adds the folded part back.
+//  * Score waves work on tile k while value waves work on tile k-1 (double-buffered LDS),
+//    with one workgroup barrier per tile.
+// LDS traffic per 32-token tile is ~76 KB against ~1.3k cycles of MFMA work per SIMD,
+// so neither LDS (~128 B/clk/CU) nor the vector memory path limits the loop.
+//
+// Rows past a sequence's end in its last page are never used: their loads are clamped to
+// the tile's first row (a valid token) and their scores masked, so NaN padding cannot
+// reach the output.  Grid: the two row blocks of one (b, u) are 8 workgroups apart so
+// that they land on the same XCD and share its L2.
+#include <math.h>
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mla {
-bool decode_absorbed_mfma_supported(const mla_shape_t&) { return false; }
-hipError_t launch_decode_absorbed_mfma(const mla_shape_t&, const void*, const void*,
-                                       const int32_t*, const int32_t*, float*, float*,
-                                       hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kD = 576;        // cache row width (d_c + d_rope)
+constexpr int kDC = 512;       // latent width
+constexpr int kPage = 64;      // tokens per page
+constexpr int kTT = 32;        // tokens per tile
+constexpr int kKS = kD / 16;   // 36 K-steps of 16 in the score contraction
+constexpr int kPRow = 40;      // P row stride in LDS (bf16): 80 B, conflict-free b128 reads
+
+// XOR swizzle of the 16-byte chunk index inside a latent tile row (64 chunks per row):
+// 8 consecutive tokens hit 8 distinct chunks (conflict-free b128 writes) and any 4
+// consecutive tokens aligned to 4 put a given 32-byte pair on 4 distinct bank groups
+// (conflict-free transposed reads).
+__device__ __forceinline__ int swz(int tok) { return ((tok & 3) << 1) | ((tok >> 2) & 1); }
+
+__device__ __forceinline__ bf16x8 load_row_chunk(const bf16_t* p) {
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return __builtin_bit_cast(bf16x8, v);
 }
+
+template <int NQ>
+struct Smem {
+  bf16_t cbuf[2][kTT * kDC];       // latent tile (swizzled rows), double buffered
+  bf16_t pbuf[2][32 * NQ * kPRow];  // P[row][token] (bf16), double buffered
+  float lfin[32 * NQ];              // final row sums
+  int restart;                      // set by a score wave when a reference must move
+};
+
+struct Work {
+  const bf16_t* q_abs;
+  const bf16_t* pool;
+  const int32_t* ptb;   // page-table row of sequence b
+  float* o_part;
+  float* lse_part;
+  size_t qrow0;         // first query row of this workgroup (global row index)
+  int lo, hi, n_tiles, T, s_q, H, y, S, u;
+  float zscale;
+  float slack;          // lazy-reference slack (log2 units)
+};
+
+// After the barrier that ends a slot every wave reads the restart flag; if it is set,
+// all waves meet twice more (everyone has read it / it has been cleared) and rerun the
+// chunk.  Every wave takes the same path, so barrier counts stay equal.
+template <typename SM>
+__device__ __forceinline__ bool check_restart(SM& sm) {
+  const bool r = __builtin_amdgcn_readfirstlane(sm.restart) != 0;
+  if (r) {
+    __syncthreads();
+    if (threadIdx.x == 0) sm.restart = 0;
+    __syncthreads();
+  }
+  return r;
+}
+
+// Score wave QW: rows [32 QW, 32 QW + 32) of the workgroup.
+template <int NQ, int QW>
+__device__ __forceinline__ void score_role(Smem<NQ>& sm, const Work& w, int lane) {
+  constexpr int KS_OWN = 32 / NQ;   // latent K-steps this wave stages for the value waves
+  const int n32 = lane & 31, g = lane >> 5;
+  bf16x8 qreg[kKS];                 // B operand: q_abs[row n32][16 ks + 8 g .. +8]
+  bf16x8 rreg[kKS];                 // A operand: cache row (token n32)[16 ks + 8 g .. +8]
+  float m_run = -INFINITY, l_run = 0.f;
+  const int r = w.y * 32 * NQ + 32 * QW + n32;     // row within the sequence: s*H + h
+  const int top_row = min(w.hi, w.T - w.s_q + r / w.H + 1);
+  // A 32-token tile never straddles a page (chunks start on page boundaries), so its
+  // page is wave-uniform and comes from a scalar load; rows past the chunk end are
+  // clamped to the tile's first row.
+  auto tile_page = [&](int k) -> int {
+    return w.ptb[__builtin_amdgcn_readfirstlane(w.lo + k * kTT) >> 6];
+  };
+  auto tile_row_ptr = [&](int k, int page) -> const bf16_t* {
+    const int t0 = __builtin_amdgcn_readfirstlane(w.lo + k * kTT);
+    const int row = (t0 & (kPage - 1)) + ((t0 + n32 < w.hi) ? n32 : 0);
+    return w.pool + (static_cast<size_t>(page) * kPage + row) * kD + 8 * g;
+  };
+  const bf16_t* qp = w.q_abs + (w.qrow0 + 32 * QW + n32) * kD + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
+  const int sw = swz(n32);
+  int cw[4];                          // byte offset of chunk 2b+g in a row, swizzled
+#pragma unroll
+  for (int b4 = 0; b4 < 4; ++b4) cw[b4] = 16 * ((2 * b4 + g) ^ sw);
+
+  bool again = true;
+  int reruns = 0;   // each rerun passes its triggering tile, so at most n_tiles happen
+  while (again) {
+    again = false;
+    l_run = 0.f;
+    int page_next = 0;    // page of tile k+1, loaded one tile ahead
+    if (w.n_tiles > 0) {
+      const bf16_t* rp = tile_row_ptr(0, tile_page(0));
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) rreg[ks] = load_row_chunk(rp + 16 * ks);
+      page_next = tile_page(min(1, w.n_tiles - 1));
+    }
+    for (int k = 0; k <= w.n_tiles; ++k) {
+      if (k < w.n_tiles) {
+        const int bi = k & 1;
+        // the last tile re-fetches itself, which keeps the load stream branch-free
+        const int kn = min(k + 1, w.n_tiles - 1);
+        const bf16_t* np = tile_row_ptr(kn, page_next);
+        page_next = tile_page(min(k + 2, w.n_tiles - 1));
+        char* crow = reinterpret_cast<char*>(&sm.cbuf[bi][n32 * kDC]);
+        f32x16 sacc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) {
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rreg[ks], qreg[ks], sacc, 0, 0, 0);
+          if (ks >= QW * KS_OWN && ks < (QW + 1) * KS_OWN)
+            // chunk 2ks+g = 8(ks/4) + (2(ks%4)+g): the swizzle only touches the low part
+            *reinterpret_cast<bf16x8*>(crow + cw[ks & 3] + 128 * (ks >> 2)) = rreg[ks];
+          rreg[ks] = load_row_chunk(np + 16 * ks);
+        }
+        // online softmax on S^T: lane holds row n32, tokens 8(j/4) + 4g + (j%4)
+        const int t0 = w.lo + k * kTT + 4 * g;
+        float z[16];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int t = t0 + 8 * (j >> 2) + (j & 3);
+          z[j] = (t < top_row) ? sacc[j] * w.zscale : -INFINITY;
+          mt = fmaxf(mt, z[j]);
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        // First visible tile of a row: take its maximum as the reference (nothing has
+        // been accumulated for the row yet).  Later, a score more than `slack` above the
+        // reference moves it and reruns the whole chunk (rare).
+        const bool move = m_run != -INFINITY && mt > m_run + w.slack;
+        if (m_run == -INFINITY || move) m_run = mt;
+        if (__builtin_amdgcn_ballot_w64(move) && reruns <= w.n_tiles) sm.restart = 1;
+        const bool live = m_run != -INFINITY;
+        bf16_t* prow = &sm.pbuf[bi][(32 * QW + n32) * kPRow];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          i16x4 pk;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = live ? exp2f(z[4 * a + i] - m_run) : 0.f;
+            l_run += p;
+            pk[i] = __builtin_bit_cast(short, static_cast<__bf16>(p));
+          }
+          *reinterpret_cast<i16x4*>(prow + 8 * a + 4 * g) = pk;
+        }
+      }
+      __syncthreads();
+      if (check_restart(sm)) {
+        again = true;
+        ++reruns;
+        break;
+      }
+    }
+  }
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (g == 0) {
+    sm.lfin[32 * QW + n32] = l_tot;
+    const size_t orow = (w.qrow0 + 32 * QW + n32) * w.S + w.u;
+    w.lse_part[orow] = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+}
+
+// One value-wave tile: acc[mb][nb] (+)= C^T[latent block mb][tile] . P^T[tile][rows nb].
+// FIRST starts the accumulators from zero, so every definition of them is an MFMA.
+template <int NQ, int MB, bool FIRST>
+__device__ __forceinline__ void value_tile(Smem<NQ>& sm, int bi, const int (&trofs)[2][2][2],
+                                           int n32, int g, f32x16 (&acc)[MB][NQ]) {
+  // B operand: P^T[token 16 kt + 8 g + i][row 32 nb + n32]
+  bf16x8 pb[2][NQ];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int nb = 0; nb < NQ; ++nb)
+      pb[kt][nb] = *reinterpret_cast<const bf16x8*>(
+          &sm.pbuf[bi][(32 * nb + n32) * kPRow + 16 * kt + 8 * g]);
+  const char* cb = reinterpret_cast<const char*>(&sm.cbuf[bi][0]);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      // A operand: C^T[latent][token] by transposed LDS reads; 16-lane group q16 gets
+      // latent rows m_base + i and tokens 16 kt + 8 g16 + (0..7).  Block mb adds
+      // 128 * (mb / 2) bytes: chunk + 8 leaves the swizzled bits alone.
+      const int ofs = 128 * (mb >> 1);
+      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(const __attribute__((address_space(3))) char*)(
+              cb + trofs[mb & 1][kt][0] + ofs));
+      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(const __attribute__((address_space(3))) char*)(
+              cb + trofs[mb & 1][kt][1] + ofs));
+      const i16x8 a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
+#pragma unroll
+      for (int nb = 0; nb < NQ; ++nb) {
+        if (FIRST && kt == 0) {
+          const f32x16 zero = {};
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kt][nb], zero, 0, 0, 0);
+        } else {
+          acc[mb][nb] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kt][nb], acc[mb][nb], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// Value wave VW: latent columns [VW * 512/NQ, (VW+1) * 512/NQ) for all 32*NQ rows.
+template <int NQ>
+__device__ __forceinline__ void value_role(Smem<NQ>& sm, const Work& w, int vw, int lane) {
+  constexpr int LAT_PV = kDC / NQ;  // latent columns per value wave
+  constexpr int MB = LAT_PV / 32;   // 32-wide M blocks
+  const int n32 = lane & 31, g = lane >> 5;
+  const int lat0 = vw * LAT_PV;
+  const int q16 = lane >> 4, L = lane & 15;
+  const int m_base = 16 * (q16 & 1), g16 = q16 >> 1;
+  // byte offsets of this lane's transposed-read chunks for M blocks 0/1, both K-steps
+  // and both token quartets
+  int trofs[2][2][2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int h4 = 0; h4 < 2; ++h4) {
+        const int col = lat0 + 32 * par + m_base + 4 * (L & 3);
+        const int tok = 16 * kt + 8 * g16 + 4 * h4 + (L >> 2);
+        trofs[par][kt][h4] = tok * (kDC * 2) + (((col >> 3) ^ swz(tok)) * 16) + (col & 7) * 2;
+      }
+  while (true) {
+    // slot 0: the score waves compute tile 0
+    __syncthreads();
+    if (check_restart(sm)) continue;
+    if (w.n_tiles == 0) {
+      __syncthreads();   // the score waves have published the row sums
+      float* orow0 = w.o_part + (w.qrow0 * w.S + w.u) * kDC + lat0 + 4 * g;
+      for (int nb = 0; nb < NQ; ++nb)
+        for (int c = 0; c < LAT_PV; c += 8)
+          *reinterpret_cast<float4*>(orow0 + (32 * nb + n32) * w.S * kDC + c) =
+              make_float4(0.f, 0.f, 0.f, 0.f);
+      return;
+    }
+    // slot 1: tile 0, accumulators start from zero
+    f32x16 acc[MB][NQ];
+    value_tile<NQ, MB, true>(sm, 0, trofs, n32, g, acc);
+    __syncthreads();
+    if (check_restart(sm)) continue;
+    bool restarted = false;
+    for (int k = 2; k <= w.n_tiles; ++k) {
+      value_tile<NQ, MB, false>(sm, (k - 1) & 1, trofs, n32, g, acc);
+      __syncthreads();
+      if (check_restart(sm)) {
+        restarted = true;
+        break;
+      }
+    }
+    if (restarted) continue;
+    __syncthreads();   // the score waves have published the row sums
+#pragma unroll
+    for (int nb = 0; nb < NQ; ++nb) {
+      const float l = sm.lfin[32 * nb + n32];
+      const float inv = (l > 0.f) ? 1.f / l : 0.f;
+      float* orow = w.o_part + ((w.qrow0 + 32 * nb + n32) * w.S + w.u) * kDC + lat0 + 4 * g;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          float4 v;
+          v.x = acc[mb][nb][4 * a + 0] * inv;
+          v.y = acc[mb][nb][4 * a + 1] * inv;
+          v.z = acc[mb][nb][4 * a + 2] * inv;
+          v.w = acc[mb][nb][4 * a + 3] * inv;
+          *reinterpret_cast<float4*>(orow + 32 * mb + 8 * a) = v;
+        }
+    }
+    return;
+  }
+}
+
+template <int NQ>
+__global__ __launch_bounds__(128 * NQ, 1) void decode_absorbed_mfma_rows32_kernel(
+    const bf16_t* __restrict__ q_abs, const bf16_t* __restrict__ pool,
+    const int32_t* __restrict__ pt, const int32_t* __restrict__ lens,
+    float* __restrict__ o_part, float* __restrict__ lse_part, int s_q, int H, int max_pages,
+    int S, int split_tokens, float zscale, float slack, int n_units, int n_yblk) {
+  __shared__ __attribute__((aligned(16))) Smem<NQ> sm;
+  const int wg = blockIdx.x;
+  const int rest = wg >> 3;
+  const int y = rest % n_yblk;
+  const int unit = (rest / n_yblk) * 8 + (wg & 7);
+  if (unit >= n_units) return;  // uniform for the whole workgroup, before any barrier
+  Work w;
+  const int b = unit / S;
+  w.u = unit - b * S;
+  w.T = lens[b];
+  split_range(w.T, w.u, S, kPage, split_tokens, w.lo, w.hi);
+  w.n_tiles = (w.hi > w.lo) ? (w.hi - w.lo + kTT - 1) / kTT : 0;
+  w.q_abs = q_abs;
+  w.pool = pool;
+  w.ptb = pt + static_cast<size_t>(b) * max_pages;
+  w.o_part = o_part;
+  w.lse_part = lse_part;
+  w.qrow0 = static_cast<size_t>(b) * s_q * H + static_cast<size_t>(y) * 32 * NQ;
+  w.s_q = s_q;
+  w.H = H;
+  w.y = y;
+  w.S = S;
+  w.zscale = zscale;
+  w.slack = slack;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) sm.restart = 0;
+  __syncthreads();
+  if (wave == 0)
+    score_role<NQ, 0>(sm, w, lane);
+  else if (NQ == 2 && wave == 1)
+    score_role<NQ, (NQ == 2 ? 1 : 0)>(sm, w, lane);
+  else
+    value_role<NQ>(sm, w, wave - NQ, lane);
+}
+
+
+// ====================================================================================
+// 64-row kernel: latent tiles staged through a 4-deep LDS ring by direct-to-LDS loads.
+//
+// Per 32-token tile every wave issues 9 of the tile's 36 wave-wide global_load_lds
+// instructions (1 KB contiguous each, so the vector memory path moves whole cache lines)
+// two tiles ahead of use.  The ring keeps raw cache rows, 16-byte chunks XOR-swizzled
+// within groups of 8 per row; both the score waves' 128-bit operand reads and the value
+// waves' transposed reads are bank-conflict free on it.  Score waves (rows 0-31 and
+// 32-63) read their A operand from the ring, so they hold only q_abs in registers; the
+// value waves read the latent columns of the same ring tile one slot later.
+// ====================================================================================
+namespace ring {
+
+constexpr int kRowB = kD * 2;              // 1152 bytes per cache row
+constexpr int kTileB = kTT * kRowB;        // 36864 bytes per tile
+constexpr int kNB = 4;                     // ring depth in tiles
+constexpr int kAhead = 2;                  // tiles loaded ahead of the score waves
+constexpr int kDmaPerWave = kTileB / 1024 / 4;   // 9 of 36 1-KB loads per tile per wave
+
+struct Smem {
+  char ring[kNB][kTileB];
+  bf16_t pbuf[2][64 * kPRow];
+  float lfin[64];
+  int restart;
+};
+
+__device__ __forceinline__ void wait_vm(bool more) {
+  // the only vector-memory loads in flight are the ring loads of the next tiles
+  if (more)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerWave) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Wave `wave` issues its share of tile kt's loads into ring slot kt % kNB.  Slot byte
+// 16*c holds chunk (c % 72) ^ swz(c / 72) of tile row c / 72; rows past the chunk end
+// repeat the tile's first row (valid data, masked later).
+__device__ __forceinline__ void load_tile(Smem& sm, const Work& w, int kt, int wave,
+                                          int lane) {
+  const int t0 = __builtin_amdgcn_readfirstlane(w.lo + kt * kTT);
+  const int page = w.ptb[t0 >> 6];
+  const bf16_t* base = w.pool + (static_cast<size_t>(page) * kPage + (t0 & (kPage - 1))) * kD;
+  char* dst = &sm.ring[kt & (kNB - 1)][0];
+  // recompute the per-lane slot math here instead of keeping 9 sets of it live
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j) {
+    const int i = wave + 4 * j;                    // 1-KB block of the tile
+    const int c = i * 64 + ln;                     // 16-byte slot of the tile
+    const int row = c / 72;
+    const int chunk = (c - row * 72) ^ swz(row);
+    const int src_row = (t0 + row < w.hi) ? row : 0;
+    __builtin_amdgcn_global_load_lds(
+        base + src_row * kD + chunk * 8,
+        (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <bool MASK>
+__device__ __forceinline__ void softmax_tile(const f32x16& sacc, int lim, float zscale,
+                                             float slack, float& m_ref, float& l_run,
+                                             bool& move, bf16_t* prow, int g) {
+  // lane holds tokens 8(j/4) + 4g + (j%4) of the tile for its row; lim = visible count
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const bool vis = !MASK || (8 * (j >> 2) + 4 * g + (j & 3) < lim);
+    mx = fmaxf(mx, vis ? sacc[j] : -INFINITY);
+  }
+  const float mt = xhalf_max(mx * zscale);
+  // first visible tile of a row fixes its reference; a later jump beyond the slack
+  // moves it and reruns the chunk
+  move = m_ref != -INFINITY && mt > m_ref + slack;
+  // a move raises the reference to this tile's maximum, so the rerun of tiles 0..k
+  // cannot trigger it again: every rerun strictly raises some row's reference
+  if (m_ref == -INFINITY || move) m_ref = mt;
+  const bool live = m_ref != -INFINITY;
+  const float nm = -m_ref;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * a + i;
+      const bool vis = !MASK || (8 * a + 4 * g + i < lim);
+      p[i] = (live && vis) ? __builtin_amdgcn_exp2f(fmaf(sacc[j], zscale, nm)) : 0.f;
+      l_run += p[i];
+    }
+    i16x4 pk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pk[i] = __builtin_bit_cast(short, static_cast<__bf16>(p[i]));
+    *reinterpret_cast<i16x4*>(prow + 8 * a + 4 * g) = pk;
+  }
+}
+
+// Score wave QW (rows 32 QW .. 32 QW + 31).
+template <int QW>
+__device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
+  const int n32 = lane & 31, g = lane >> 5;
+  bf16x8 qreg[kKS];
+  const int r = w.y * 64 + 32 * QW + n32;
+  const int top_row = min(w.hi, w.T - w.s_q + r / w.H + 1);
+  const bf16_t* qp = w.q_abs + (w.qrow0 + 32 * QW + n32) * kD + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
+  const int sw = swz(n32);
+  int rb[4];                         // byte offset of chunk 2b+g of this lane's row
+#pragma unroll
+  for (int b4 = 0; b4 < 4; ++b4) rb[b4] = n32 * kRowB + 16 * ((2 * b4 + g) ^ sw);
+  float m_ref = -INFINITY, l_run = 0.f;
+  int reruns = 0;   // each rerun passes its triggering tile, so at most n_tiles happen
+  while (true) {
+    l_run = 0.f;
+    if (w.n_tiles > 0) load_tile(sm, w, 0, QW, lane);
+    if (w.n_tiles > 1) load_tile(sm, w, 1, QW, lane);
+    wait_vm(w.n_tiles > 1);
+    __syncthreads();
+    bool restarted = false;
+    for (int k = 0; k <= w.n_tiles; ++k) {
+      const bool more = k + kAhead < w.n_tiles;
+      if (more) load_tile(sm, w, k + kAhead, QW, lane);
+      if (k < w.n_tiles) {
+        const char* tb = &sm.ring[k & (kNB - 1)][0];
+        f32x16 sacc = {};
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) {
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8*>(tb + rb[ks & 3] + 128 * (ks >> 2));
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc, 0, 0, 0);
+        }
+        const int lim = top_row - (w.lo + k * kTT);
+        bf16_t* prow = &sm.pbuf[k & 1][(32 * QW + n32) * kPRow];
+        bool move;
+        if (__builtin_amdgcn_ballot_w64(lim < kTT))
+          softmax_tile<true>(sacc, lim, w.zscale, w.slack, m_ref, l_run, move, prow, g);
+        else
+          softmax_tile<false>(sacc, lim, w.zscale, w.slack, m_ref, l_run, move, prow, g);
+        if (__builtin_amdgcn_ballot_w64(move) && reruns <= w.n_tiles) sm.restart = 1;
+      }
+      wait_vm(more);
+      __syncthreads();
+      if (check_restart(sm)) {
+        restarted = true;
+        break;
+      }
+    }
+    if (!restarted) break;
+    ++reruns;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  const float l_tot = xhalf_sum(l_run);
+  if (g == 0) {
+    sm.lfin[32 * QW + n32] = l_tot;
+    const size_t orow = (w.qrow0 + 32 * QW + n32) * w.S + w.u;
+    w.lse_part[orow] = (l_tot > 0.f) ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+}
+
+// One value-wave tile from ring slot `slot`: acc (+)= C^T . P^T.
+template <bool FIRST>
+__device__ __forceinline__ void value_ring_tile(Smem& sm, int slot, int pb_i,
+                                                const int (&trofs)[2][2][2], int n32, int g,
+                                                f32x16 (&acc)[8][2]) {
+  bf16x8 pb[2][2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      pb[kt][nb] = *reinterpret_cast<const bf16x8*>(
+          &sm.pbuf[pb_i][(32 * nb + n32) * kPRow + 16 * kt + 8 * g]);
+  const char* cb = &sm.ring[slot][0];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int ofs = 128 * (mb >> 1);
+      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(const __attribute__((address_space(3))) char*)(
+              cb + trofs[mb & 1][kt][0] + ofs));
+      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(const __attribute__((address_space(3))) char*)(
+              cb + trofs[mb & 1][kt][1] + ofs));
+      const i16x8 a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        if (FIRST && kt == 0) {
+          const f32x16 zero = {};
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kt][nb], zero, 0, 0, 0);
+        } else {
+          acc[mb][nb] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kt][nb], acc[mb][nb], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// Value wave VW: latent columns [256 VW, 256 VW + 256) for all 64 rows.
+__device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int vw, int lane) {
+  const int n32 = lane & 31, g = lane >> 5;
+  const int lat0 = vw * 256;
+  const int wave = 2 + vw;
+  const int q16 = lane >> 4, L = lane & 15;
+  const int m_base = 16 * (q16 & 1), g16 = q16 >> 1;
+  int trofs[2][2][2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int h4 = 0; h4 < 2; ++h4) {
+        const int col = lat0 + 32 * par + m_base + 4 * (L & 3);
+        const int tok = 16 * kt + 8 * g16 + 4 * h4 + (L >> 2);
+        trofs[par][kt][h4] = tok * kRowB + (((col >> 3) ^ swz(tok)) * 16) + (col & 7) * 2;
+      }
+  while (true) {
+    if (w.n_tiles > 0) load_tile(sm, w, 0, wave, lane);
+    if (w.n_tiles > 1) load_tile(sm, w, 1, wave, lane);
+    wait_vm(w.n_tiles > 1);
+    __syncthreads();
+    // slot 0: the score waves work on tile 0
+    bool more = kAhead < w.n_tiles;
+    if (more) load_tile(sm, w, kAhead, wave, lane);
+    wait_vm(more);
+    __syncthreads();
+    if (check_restart(sm)) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      continue;
+    }
+    if (w.n_tiles == 0) {
+      __syncthreads();
+      float* orow0 = w.o_part + (w.qrow0 * w.S + w.u) * kDC + lat0 + 4 * g;
+      for (int nb = 0; nb < 2; ++nb)
+        for (int c = 0; c < 256; c += 8)
+          *reinterpret_cast<float4*>(orow0 + (32 * nb + n32) * w.S * kDC + c) =
+              make_float4(0.f, 0.f, 0.f, 0.f);
+      return;
+    }
+    f32x16 acc[8][2];
+    bool restarted = false;
+    for (int k = 1; k <= w.n_tiles; ++k) {
+      more = k + kAhead < w.n_tiles;
+      if (more) load_tile(sm, w, k + kAhead, wave, lane);
+      if (k == 1)
+        value_ring_tile<true>(sm, 0, 0, trofs, n32, g, acc);
+      else
+        value_ring_tile<false>(sm, (k - 1) & (kNB - 1), (k - 1) & 1, trofs, n32, g, acc);
+      wait_vm(more);
+      __syncthreads();
+      if (check_restart(sm)) {
+        restarted = true;
+        break;
+      }
+    }
+    if (restarted) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      continue;
+    }
+    __syncthreads();   // the score waves have published the row sums
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float l = sm.lfin[32 * nb + n32];
+      const float inv = (l > 0.f) ? 1.f / l : 0.f;
+      float* orow = w.o_part + ((w.qrow0 + 32 * nb + n32) * w.S + w.u) * kDC + lat0 + 4 * g;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          float4 v;
+          v.x = acc[mb][nb][4 * a + 0] * inv;
+          v.y = acc[mb][nb][4 * a + 1] * inv;
+          v.z = acc[mb][nb][4 * a + 2] * inv;
+          v.w = acc[mb][nb][4 * a + 3] * inv;
+          *reinterpret_cast<float4*>(orow + 32 * mb + 8 * a) = v;
+        }
+    }
+    return;
+  }
+}
+
+}  // namespace ring
+
+__global__ __launch_bounds__(256, 1) void decode_absorbed_mfma_ring_kernel(
+    const bf16_t* __restrict__ q_abs, const bf16_t* __restrict__ pool,
+    const int32_t* __restrict__ pt, const int32_t* __restrict__ lens,
+    float* __restrict__ o_part, float* __restrict__ lse_part, int s_q, int H, int max_pages,
+    int S, int split_tokens, float zscale, float slack, int n_units, int n_yblk) {
+  __shared__ __attribute__((aligned(16))) ring::Smem sm;
+  const int wg = blockIdx.x;
+  const int rest = wg >> 3;
+  const int y = rest % n_yblk;
+  const int unit = (rest / n_yblk) * 8 + (wg & 7);
+  if (unit >= n_units) return;  // uniform for the whole workgroup, before any barrier
+  Work w;
+  const int b = unit / S;
+  w.u = unit - b * S;
+  w.T = lens[b];
+  split_range(w.T, w.u, S, kPage, split_tokens, w.lo, w.hi);
+  w.n_tiles = (w.hi > w.lo) ? (w.hi - w.lo + kTT - 1) / kTT : 0;
+  w.q_abs = q_abs;
+  w.pool = pool;
+  w.ptb = pt + static_cast<size_t>(b) * max_pages;
+  w.o_part = o_part;
+  w.lse_part = lse_part;
+  w.qrow0 = static_cast<size_t>(b) * s_q * H + static_cast<size_t>(y) * 64;
+  w.s_q = s_q;
+  w.H = H;
+  w.y = y;
+  w.S = S;
+  w.zscale = zscale;
+  w.slack = slack;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) sm.restart = 0;
+  __syncthreads();
+  if (wave == 0)
+    ring::score_wave<0>(sm, w, lane);
+  else if (wave == 1)
+    ring::score_wave<1>(sm, w, lane);
+  else
+    ring::value_wave(sm, w, wave - 2, lane);
+}
+
+}  // namespace
+
+bool decode_absorbed_mfma_supported(const mla_shape_t& s) {
+  return s.dtype == MLA_BF16 && s.d_c == kDC && s.d_rope == kD - kDC &&
+         s.page_size == kPage && (s.s_q * s.n_heads) % 32 == 0;
+}
+
+hipError_t launch_decode_absorbed_mfma(const mla_shape_t& s, const void* q_abs,
+                                       const void* pool, const int32_t* pt,
+                                       const int32_t* lens, float* o_part, float* lse_part,
+                                       hipStream_t st) {
+  const int rows = s.s_q * s.n_heads;
+  const int nq = (rows % 64 == 0) ? 2 : 1;
+  const int n_yblk = rows / (32 * nq);
+  const int n_units = s.batch * s.n_splits;
+  const unsigned grid = static_cast<unsigned>((n_units + 7) / 8) * 8u * n_yblk;
+  const float zscale = s.softmax_scale * kLog2e;
+  // Slack (log2 units) before a row's reference maximum moves; the default keeps P below
+  // 2^32.  MLA_DECODE_REF_SLACK (0..64) overrides it, e.g. 0 to exercise the rerun path.
+  float slack = 32.f;
+  if (const char* e = getenv("MLA_DECODE_REF_SLACK")) {
+    const float v = strtof(e, nullptr);
+    if (v >= 0.f && v <= 64.f) slack = v;
+  }
+  if (nq == 2)
+    hipLaunchKernelGGL(decode_absorbed_mfma_ring_kernel, dim3(grid), dim3(256), 0, st,
+                       static_cast<const bf16_t*>(q_abs), static_cast<const bf16_t*>(pool), pt,
+                       lens, o_part, lse_part, s.s_q, s.n_heads, s.max_pages, s.n_splits,
+                       s.split_tokens, zscale, slack, n_units, n_yblk);
+  else
+    hipLaunchKernelGGL(decode_absorbed_mfma_rows32_kernel<1>, dim3(grid), dim3(128), 0, st,
+                       static_cast<const bf16_t*>(q_abs), static_cast<const bf16_t*>(pool), pt,
+                       lens, o_part, lse_part, s.s_q, s.n_heads, s.max_pages, s.n_splits,
+                       s.split_tokens, zscale, slack, n_units, n_yblk);
+  return hipGetLastError();
+}
+
 }  // namespace mla

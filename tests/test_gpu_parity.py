@@ -287,3 +287,34 @@ def test_full_long_b4_t131072():
 
 def test_full_mtp_b64_ragged():
     sampled_full_check(get_config("mtp-b64-ragged"), [0, 17, 40, 63], [0, 127, 77])
+
+
+# ------------------------------------------- reference moves (online-softmax fold path)
+
+@pytest.mark.parametrize("slack", ["0", "0.25"])
+def test_reference_moves_fold_path(slack, monkeypatch):
+    """With no slack the per-row reference moves whenever a tile raises the maximum, so
+    the matrix-core kernel folds its accumulators into o_part on most tiles."""
+    monkeypatch.setenv("MLA_DECODE_REF_SLACK", slack)
+    cfg = small(batch=3, s_q=2, ctx=("list", [1500, 700, 65]))
+    errs = check_absorbed_all_steps(make_inputs(cfg, seed=12), S=3)
+    assert errs["out"] <= TOL["bf16"]
+
+
+def test_growing_scores_move_the_reference_by_large_steps():
+    """Scores that climb by ~38 log2 units per tile move the reference at the default
+    slack on every tile; the result must still match the oracle."""
+    cfg = small(batch=2, ctx=("list", [2000, 900]), n_splits=3)
+    inp = make_inputs(cfg, seed=13)
+    inp.q[...] = 0.0
+    inp.q[..., cfg.d_nope] = 40.0                       # only the first RoPE coordinate
+    pool = inp.pool_f32().copy()
+    for b in range(cfg.batch):
+        for i, p in enumerate(inp.page_table[b]):
+            if p < 0:
+                continue
+            t = i * cfg.page_size + np.arange(cfg.page_size)
+            pool[p, :, cfg.d_c] = (t // 32) * 16.0        # exact in bf16
+    from workloads.gen import bf16_bits
+    inp.pool = bf16_bits(pool)
+    check_absorbed_all_steps(inp)
