@@ -65,6 +65,15 @@ constexpr int kPRow = 40;      // P row stride in LDS (bf16): 80 B, conflict-fre
 // (conflict-free transposed reads).
 __device__ __forceinline__ int swz(int tok) { return ((tok & 3) << 1) | ((tok >> 2) & 1); }
 
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt and lgkmcnt left at their "no wait" maxima).  The builtin, unlike inline
+// asm, is seen by the compiler's own wait insertion, which then adds no redundant waits.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
 __device__ __forceinline__ bf16x8 load_row_chunk(const bf16_t* p) {
   u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return __builtin_bit_cast(bf16x8, v);
@@ -371,15 +380,19 @@ __global__ __launch_bounds__(128 * NQ, 1) void decode_absorbed_mfma_rows32_kerne
 
 
 // ====================================================================================
-// 64-row kernel: latent tiles staged through a 4-deep LDS ring by direct-to-LDS loads.
+// 64-row kernel: latent tiles staged through a 4-tile LDS ring by direct-to-LDS loads.
 //
-// Per 32-token tile every wave issues 9 of the tile's 36 wave-wide global_load_lds
-// instructions (1 KB contiguous each, so the vector memory path moves whole cache lines)
-// two tiles ahead of use.  The ring keeps raw cache rows, 16-byte chunks XOR-swizzled
-// within groups of 8 per row; both the score waves' 128-bit operand reads and the value
-// waves' transposed reads are bank-conflict free on it.  Score waves (rows 0-31 and
-// 32-63) read their A operand from the ring, so they hold only q_abs in registers; the
-// value waves read the latent columns of the same ring tile one slot later.
+// Every wave issues 9 of a 32-token tile's 36 wave-wide global_load_lds_dwordx4
+// instructions (1 KB contiguous each, so the vector memory path moves whole cache lines),
+// two tiles ahead of use.  They are issued from inline asm: the compiler then does not
+// treat them as LDS stores in flight, so it adds no waits of its own before ring reads;
+// instead every wave waits for its own loads of the next tile (vmcnt) before the slot's
+// barrier.  A DMA load has no destination registers, so nothing in flight can overwrite
+// a register.  The ring keeps raw cache rows with 16-byte chunks XOR-swizzled within
+// groups of 8 per row; the score waves' 128-bit operand reads and the value waves'
+// transposed reads are bank-conflict free on it.  Score waves (rows 0-31 and 32-63) read
+// their A operand from the ring and hold only q_abs in registers; the value waves read
+// the latent columns of the same tile one slot later.
 // ====================================================================================
 namespace ring {
 
@@ -396,36 +409,35 @@ struct Smem {
   int restart;
 };
 
-__device__ __forceinline__ void wait_vm(bool more) {
-  // the only vector-memory loads in flight are the ring loads of the next tiles
-  if (more)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerWave) : "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_block) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_block) : "memory", "m0");
 }
 
-// Wave `wave` issues its share of tile kt's loads into ring slot kt % kNB.  Slot byte
-// 16*c holds chunk (c % 72) ^ swz(c / 72) of tile row c / 72; rows past the chunk end
-// repeat the tile's first row (valid data, masked later).
-__device__ __forceinline__ void load_tile(Smem& sm, const Work& w, int kt, int wave,
-                                          int lane) {
+// Ring byte 16*c of a tile holds chunk (c % 72) ^ swz(c / 72) of tile row c / 72; load j
+// of wave `wave` moves ring bytes [1024 (wave + 4 j), +1024), 16 per lane.
+// Wave `wave`'s share of tile kt into ring slot kt % kNB.  Rows past the chunk end (only
+// in a chunk's last tile) read the tile's first row instead: valid data, masked later.
+__device__ __forceinline__ void load_tile(Smem& sm, const Work& w, int lane, int kt, int wave) {
   const int t0 = __builtin_amdgcn_readfirstlane(w.lo + kt * kTT);
   const int page = w.ptb[t0 >> 6];
   const bf16_t* base = w.pool + (static_cast<size_t>(page) * kPage + (t0 & (kPage - 1))) * kD;
-  char* dst = &sm.ring[kt & (kNB - 1)][0];
-  // recompute the per-lane slot math here instead of keeping 9 sets of it live
+  const int valid = w.hi - t0;
+  const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) char*)(&sm.ring[kt & (kNB - 1)][0])));
+  // the per-load offsets are recomputed from an opaque lane id on every call: a handful
+  // of ALU ops, instead of nine registers held across the whole chunk loop
   int ln = lane;
   asm volatile("" : "+v"(ln));
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j) {
-    const int i = wave + 4 * j;                    // 1-KB block of the tile
-    const int c = i * 64 + ln;                     // 16-byte slot of the tile
+    const int c = (wave + 4 * j) * 64 + ln;
     const int row = c / 72;
-    const int chunk = (c - row * 72) ^ swz(row);
-    const int src_row = (t0 + row < w.hi) ? row : 0;
-    __builtin_amdgcn_global_load_lds(
-        base + src_row * kD + chunk * 8,
-        (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+    // rows past the chunk end (only in its last tile) read the tile's first row instead:
+    // valid data, masked later
+    const int o = (row < valid) ? row * kD + ((c - row * 72) ^ swz(row)) * 8
+                                : ((c - row * 72) ^ swz(row)) * 8;
+    dma16(base + o, __builtin_amdgcn_readfirstlane(dst + (wave + 4 * j) * 1024));
   }
 }
 
@@ -453,11 +465,10 @@ __device__ __forceinline__ void softmax_tile(const f32x16& sacc, int lim, float 
     mx = fmaxf(mx, vis ? sacc[j] : -INFINITY);
   }
   const float mt = xhalf_max(mx * zscale);
-  // first visible tile of a row fixes its reference; a later jump beyond the slack
-  // moves it and reruns the chunk
+  // First visible tile of a row fixes its reference; a later jump beyond the slack
+  // raises it to this tile's maximum and reruns the chunk, so the rerun cannot trigger
+  // again at this tile: every rerun strictly raises some row's reference.
   move = m_ref != -INFINITY && mt > m_ref + slack;
-  // a move raises the reference to this tile's maximum, so the rerun of tiles 0..k
-  // cannot trigger it again: every rerun strictly raises some row's reference
   if (m_ref == -INFINITY || move) m_ref = mt;
   const bool live = m_ref != -INFINITY;
   const float nm = -m_ref;
@@ -478,7 +489,7 @@ __device__ __forceinline__ void softmax_tile(const f32x16& sacc, int lim, float 
   }
 }
 
-// Score wave QW (rows 32 QW .. 32 QW + 31).
+// Score wave QW (rows 32 QW .. 32 QW + 31).  Slot k: scores and P of tile k.
 template <int QW>
 __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
   const int n32 = lane & 31, g = lane >> 5;
@@ -488,6 +499,9 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
   const bf16_t* qp = w.q_abs + (w.qrow0 + 32 * QW + n32) * kD + 8 * g;
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
+  // q_abs has landed before any ring load is issued, so the compiler's view of the
+  // vector-memory counter stays exact (it does not see the asm ring loads)
+  wait_vmcnt<0>();
   const int sw = swz(n32);
   int rb[4];                         // byte offset of chunk 2b+g of this lane's row
 #pragma unroll
@@ -496,22 +510,35 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
   int reruns = 0;   // each rerun passes its triggering tile, so at most n_tiles happen
   while (true) {
     l_run = 0.f;
-    if (w.n_tiles > 0) load_tile(sm, w, 0, QW, lane);
-    if (w.n_tiles > 1) load_tile(sm, w, 1, QW, lane);
-    wait_vm(w.n_tiles > 1);
+    if (w.n_tiles > 0) load_tile(sm, w, lane, 0, QW);
+    if (w.n_tiles > 1) load_tile(sm, w, lane, 1, QW);
+    if (w.n_tiles > 1) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
     __syncthreads();
     bool restarted = false;
     for (int k = 0; k <= w.n_tiles; ++k) {
       const bool more = k + kAhead < w.n_tiles;
-      if (more) load_tile(sm, w, k + kAhead, QW, lane);
+      if (more) load_tile(sm, w, lane, k + kAhead, QW);
       if (k < w.n_tiles) {
         const char* tb = &sm.ring[k & (kNB - 1)][0];
         f32x16 sacc = {};
+        // A operands run kPF K-steps ahead of the MFMA that consumes them
+        constexpr int kPF = 8;
+        bf16x8 abuf[kPF];
+#pragma unroll
+        for (int ks = 0; ks < kPF; ++ks)
+          abuf[ks] = *reinterpret_cast<const bf16x8*>(tb + rb[ks & 3] + 128 * (ks >> 2));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < kKS; ++ks) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(tb + rb[ks & 3] + 128 * (ks >> 2));
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abuf[ks % kPF], qreg[ks], sacc, 0,
+                                                         0, 0);
+          if (ks + kPF < kKS) {
+            const int kn = ks + kPF;
+            abuf[ks % kPF] =
+                *reinterpret_cast<const bf16x8*>(tb + rb[kn & 3] + 128 * (kn >> 2));
+          }
+          // keep the read for step ks+kPF between MFMAs ks and ks+1
+          __builtin_amdgcn_sched_barrier(0);
         }
         const int lim = top_row - (w.lo + k * kTT);
         bf16_t* prow = &sm.pbuf[k & 1][(32 * QW + n32) * kPRow];
@@ -522,7 +549,8 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
           softmax_tile<false>(sacc, lim, w.zscale, w.slack, m_ref, l_run, move, prow, g);
         if (__builtin_amdgcn_ballot_w64(move) && reruns <= w.n_tiles) sm.restart = 1;
       }
-      wait_vm(more);
+      // this wave's loads of tile k+1 have landed (only tile k+2's may be in flight)
+      if (more) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
       __syncthreads();
       if (check_restart(sm)) {
         restarted = true;
@@ -531,7 +559,7 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
     }
     if (!restarted) break;
     ++reruns;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmcnt<0>();
   }
   const float l_tot = xhalf_sum(l_run);
   if (g == 0) {
@@ -542,7 +570,8 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
   __syncthreads();
 }
 
-// One value-wave tile from ring slot `slot`: acc (+)= C^T . P^T.
+// One value-wave tile from ring slot `slot`: acc (+)= C^T . P^T.  The transposed
+// A-operand reads run four (mb, kt) steps ahead of their MFMA pair.
 template <bool FIRST>
 __device__ __forceinline__ void value_ring_tile(Smem& sm, int slot, int pb_i,
                                                 const int (&trofs)[2][2][2], int n32, int g,
@@ -555,38 +584,61 @@ __device__ __forceinline__ void value_ring_tile(Smem& sm, int slot, int pb_i,
       pb[kt][nb] = *reinterpret_cast<const bf16x8*>(
           &sm.pbuf[pb_i][(32 * nb + n32) * kPRow + 16 * kt + 8 * g]);
   const char* cb = &sm.ring[slot][0];
+  // the 8 base offsets, opaque per tile, so that their per-block variants are formed
+  // here (one add each) rather than kept live across the loop
+  int to[2][2][2];
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) {
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int ofs = 128 * (mb >> 1);
-      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(const __attribute__((address_space(3))) char*)(
-              cb + trofs[mb & 1][kt][0] + ofs));
-      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(const __attribute__((address_space(3))) char*)(
-              cb + trofs[mb & 1][kt][1] + ofs));
-      const i16x8 a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        if (FIRST && kt == 0) {
-          const f32x16 zero = {};
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kt][nb], zero, 0, 0, 0);
-        } else {
-          acc[mb][nb] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kt][nb], acc[mb][nb], 0, 0, 0);
-        }
+      for (int c = 0; c < 2; ++c) {
+        to[a][b][c] = trofs[a][b][c];
+        asm volatile("" : "+v"(to[a][b][c]));
+      }
+  auto read_a = [&](int step) -> bf16x8 {
+    const int mb = step >> 1, kt = step & 1;
+    const int ofs = 128 * (mb >> 1);
+    const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(const __attribute__((address_space(3))) char*)(
+            cb + to[mb & 1][kt][0] + ofs));
+    const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(const __attribute__((address_space(3))) char*)(
+            cb + to[mb & 1][kt][1] + ofs));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  constexpr int kSteps = 16, kPF = 4;
+  bf16x8 abuf[kPF];
+#pragma unroll
+  for (int st = 0; st < kPF; ++st) abuf[st] = read_a(st);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st) {
+    const int mb = st >> 1, kt = st & 1;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      if (FIRST && kt == 0) {
+        const f32x16 zero = {};
+        acc[mb][nb] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(abuf[st % kPF], pb[kt][nb], zero, 0, 0, 0);
+      } else {
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abuf[st % kPF], pb[kt][nb],
+                                                              acc[mb][nb], 0, 0, 0);
       }
     }
+    if (st + kPF < kSteps) abuf[st % kPF] = read_a(st + kPF);
+    // keep the reads for step st+kPF between MFMA pairs st and st+1
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Value wave VW: latent columns [256 VW, 256 VW + 256) for all 64 rows.
-__device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int vw, int lane) {
+// Value wave VW: latent columns [256 VW, 256 VW + 256) for all 64 rows.  Slot k: its
+// share of tile k+2's loads, then the value product of tile k-1.
+template <int VW>
+__device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
   const int n32 = lane & 31, g = lane >> 5;
-  const int lat0 = vw * 256;
-  const int wave = 2 + vw;
+  constexpr int lat0 = VW * 256;
+  constexpr int wave = 2 + VW;
   const int q16 = lane >> 4, L = lane & 15;
   const int m_base = 16 * (q16 & 1), g16 = q16 >> 1;
   int trofs[2][2][2];
@@ -600,22 +652,23 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int vw, int 
         const int tok = 16 * kt + 8 * g16 + 4 * h4 + (L >> 2);
         trofs[par][kt][h4] = tok * kRowB + (((col >> 3) ^ swz(tok)) * 16) + (col & 7) * 2;
       }
+  const int n = w.n_tiles;
   while (true) {
-    if (w.n_tiles > 0) load_tile(sm, w, 0, wave, lane);
-    if (w.n_tiles > 1) load_tile(sm, w, 1, wave, lane);
-    wait_vm(w.n_tiles > 1);
+    if (n > 0) load_tile(sm, w, lane, 0, wave);
+    if (n > 1) load_tile(sm, w, lane, 1, wave);
+    if (n > 1) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
     __syncthreads();
     // slot 0: the score waves work on tile 0
-    bool more = kAhead < w.n_tiles;
-    if (more) load_tile(sm, w, kAhead, wave, lane);
-    wait_vm(more);
+    bool more = kAhead < n;
+    if (more) load_tile(sm, w, lane, kAhead, wave);
+    if (more) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
     __syncthreads();
     if (check_restart(sm)) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wait_vmcnt<0>();
       continue;
     }
-    if (w.n_tiles == 0) {
-      __syncthreads();
+    if (n == 0) {
+      __syncthreads();   // the score waves have published the row sums
       float* orow0 = w.o_part + (w.qrow0 * w.S + w.u) * kDC + lat0 + 4 * g;
       for (int nb = 0; nb < 2; ++nb)
         for (int c = 0; c < 256; c += 8)
@@ -623,24 +676,24 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int vw, int 
               make_float4(0.f, 0.f, 0.f, 0.f);
       return;
     }
+    // slot 1 (peeled, so the accumulators are first written outside the loop)
     f32x16 acc[8][2];
-    bool restarted = false;
-    for (int k = 1; k <= w.n_tiles; ++k) {
-      more = k + kAhead < w.n_tiles;
-      if (more) load_tile(sm, w, k + kAhead, wave, lane);
-      if (k == 1)
-        value_ring_tile<true>(sm, 0, 0, trofs, n32, g, acc);
-      else
-        value_ring_tile<false>(sm, (k - 1) & (kNB - 1), (k - 1) & 1, trofs, n32, g, acc);
-      wait_vm(more);
+    more = 1 + kAhead < n;
+    if (more) load_tile(sm, w, lane, 1 + kAhead, wave);
+    value_ring_tile<true>(sm, 0, 0, trofs, n32, g, acc);
+    if (more) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
+    __syncthreads();
+    bool restarted = check_restart(sm);
+    for (int k = 2; k <= n && !restarted; ++k) {
+      more = k + kAhead < n;
+      if (more) load_tile(sm, w, lane, k + kAhead, wave);
+      value_ring_tile<false>(sm, (k - 1) & (kNB - 1), (k - 1) & 1, trofs, n32, g, acc);
+      if (more) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
       __syncthreads();
-      if (check_restart(sm)) {
-        restarted = true;
-        break;
-      }
+      restarted = check_restart(sm);
     }
     if (restarted) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wait_vmcnt<0>();
       continue;
     }
     __syncthreads();   // the score waves have published the row sums
@@ -653,6 +706,8 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int vw, int 
       for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
+          // a few accumulators at a time, so the epilogue needs only a few VGPRs
+          __builtin_amdgcn_sched_barrier(0);
           float4 v;
           v.x = acc[mb][nb][4 * a + 0] * inv;
           v.y = acc[mb][nb][4 * a + 1] * inv;
@@ -667,7 +722,10 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int vw, int 
 
 }  // namespace ring
 
-__global__ __launch_bounds__(256, 1) void decode_absorbed_mfma_ring_kernel(
+// One workgroup per CU (the ring takes 158 KB of LDS), so the scheduler may use the
+// whole register file of each SIMD for operand prefetch.
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_absorbed_mfma_ring_kernel(
     const bf16_t* __restrict__ q_abs, const bf16_t* __restrict__ pool,
     const int32_t* __restrict__ pt, const int32_t* __restrict__ lens,
     float* __restrict__ o_part, float* __restrict__ lse_part, int s_q, int H, int max_pages,
@@ -703,8 +761,10 @@ __global__ __launch_bounds__(256, 1) void decode_absorbed_mfma_ring_kernel(
     ring::score_wave<0>(sm, w, lane);
   else if (wave == 1)
     ring::score_wave<1>(sm, w, lane);
+  else if (wave == 2)
+    ring::value_wave<0>(sm, w, lane);
   else
-    ring::value_wave(sm, w, wave - 2, lane);
+    ring::value_wave<1>(sm, w, lane);
 }
 
 }  // namespace
