@@ -47,6 +47,8 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--extra", action="store_true",
                     help="also time the other workloads (stderr lines)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not flush the last-level cache between steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -92,8 +94,24 @@ def cpu_baseline(inp, seconds):
                       f"{el:.1f} s, scaled to all {c.batch}x{c.n_heads} rows"}
 
 
-def time_workload(name, steps, warmup, splits=None):
+FLUSH_BYTES = 1 << 30   # > the 256 MB Infinity Cache: every step starts from HBM
+
+
+def _flusher():
+    import torch
+    buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    return lambda: buf.fill_(1.0)
+
+
+def _stats(ms):
     import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return float(np.median(a)), float(np.percentile(a, 10)), float(np.percentile(a, 90))
+
+
+def time_workload(name, steps, warmup, splits=None, flush=True):
+    """Absorbed step a1 -> a2 -> a3 -> a4; HIP events between the kernels of every step,
+    with the last-level cache flushed between steps (outside the events)."""
     import torch
     import head_latent_attention_02_amd as mla
     from workloads import get_config, make_inputs
@@ -108,31 +126,92 @@ def time_workload(name, steps, warmup, splits=None):
     op = d.o_part_view(cfg.d_c)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
+    fl = _flusher() if flush else (lambda: None)
 
     def step(ev=None):
+        rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
+        rec(0)
         mla.mla_absorb_q(sh, d.q, d.w_uk, d.q_abs, stream=sp)
-        if ev:
-            ev[0].record(stream)
+        rec(1)
         mla.mla_decode_absorbed(sh, d.q_abs, d.pool, d.page_table, d.ctx_lens, op,
                                 d.lse_part, stream=sp)
-        if ev:
-            ev[1].record(stream)
+        rec(2)
         mla.mla_splitkv_combine(sh, cfg.d_c, op, d.lse_part, d.o_lat, d.lse, stream=sp)
+        rec(3)
         mla.mla_out_uv(sh, d.o_lat, d.w_uv, d.out, stream=sp)
+        rec(4)
 
     for _ in range(warmup):
+        fl()
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        fl()
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    return inp, d, wall / steps * 1e3, dec_ms
+    ms = {"step": [e[0].elapsed_time(e[4]) for e in evs],
+          "absorb_q": [e[0].elapsed_time(e[1]) for e in evs],
+          "decode": [e[1].elapsed_time(e[2]) for e in evs],
+          "combine": [e[2].elapsed_time(e[3]) for e in evs],
+          "out_uv": [e[3].elapsed_time(e[4]) for e in evs]}
+    return inp, d, ms, wall / steps * 1e3
+
+
+def time_gqa_path(name, steps, warmup, flush=True):
+    """GQA path on the expanded per-group cache: a5 -> a3 (a6 runs once, untimed)."""
+    import torch
+    import head_latent_attention_02_amd as mla
+    from workloads import get_config, make_inputs
+    from workloads.device import DeviceInputs
+
+    cfg = get_config(name)
+    inp = make_inputs(cfg)
+    d = DeviceInputs(inp)
+    sh = d.shape
+    n = inp.num_pages
+    k = torch.empty(n, cfg.page_size, cfg.n_wheads, cfg.d_nope, dtype=torch.bfloat16,
+                    device="cuda")
+    v = torch.empty(n, cfg.page_size, cfg.n_wheads, cfg.d_v, dtype=torch.bfloat16,
+                    device="cuda")
+    kr = torch.empty(n, cfg.page_size, cfg.d_rope, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    mla.gqla_expand_cache(sh, d.pool, d.w_uk, d.w_uv, k, v, kr, stream=sp)
+    del d.pool
+    op = d.o_part_view(cfg.d_v)
+    fl = _flusher() if flush else (lambda: None)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        mla.gqla_decode_gqa(sh, d.q, k, v, kr, d.page_table, d.ctx_lens, op, d.lse_part,
+                            stream=sp)
+        if ev:
+            ev[1].record(stream)
+        mla.mla_splitkv_combine(sh, cfg.d_v, op, d.lse_part, d.out, d.lse, stream=sp)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        fl()
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        fl()
+        step(evs[i])
+    torch.cuda.synchronize()
+    dec = _stats([e[0].elapsed_time(e[1]) for e in evs])[0]
+    core = _stats([e[0].elapsed_time(e[2]) for e in evs])[0]
+    bpt = mla.gqla_cache_scalars_per_token(sh) * 2
+    return {"workload": name, "path": "gqa", "decode_ms": dec, "core_ms": core,
+            "tokens_per_s": inp.total_tokens / (core * 1e-3),
+            "decode_GBs": inp.total_tokens * bpt / (dec * 1e-3) / 1e9,
+            "kernel": "mfma" if mla.gqla_decode_kernel_kind(sh) == 1 else "generic"}
 
 
 def main():
@@ -146,7 +225,10 @@ def main():
         return
     import head_latent_attention_02_amd as mla
 
-    inp, d, ms_step, dec_ms = time_workload(args.workload, args.steps, args.warmup, args.splits)
+    inp, d, ms, wall_ms = time_workload(args.workload, args.steps, args.warmup, args.splits,
+                                        flush=not args.no_flush)
+    ms_step, p10, p90 = _stats(ms["step"])
+    dec_ms = _stats(ms["decode"])[0]
     c = inp.cfg
     tokens = inp.total_tokens
     dec_bytes = tokens * c.D * 2                                  # algorithmic cache bytes
@@ -170,7 +252,11 @@ def main():
                    "s_q": c.s_q, "heads": c.n_heads, "d_c": c.d_c, "d_rope": c.d_rope,
                    "n_splits": d.shape.n_splits, "page_size": c.page_size,
                    "path": "absorbed", "kernel": "mfma" if mla.mla_decode_kernel_kind(d.shape)
-                   == 1 else "generic"},
+                   == 1 else "generic", "llc_flush_between_steps": not args.no_flush},
+        "step_ms_p10_p90": [p10, p90],
+        "kernel_ms": {k: _stats(v)[0] for k, v in ms.items() if k != "step"},
+        "core_ms": _stats([a + b for a, b in zip(ms["decode"], ms["combine"])])[0],
+        "wall_ms_per_step_incl_flush": wall_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "mla_decode_absorbed", "kernel_ms": dec_ms,
@@ -183,13 +269,21 @@ def main():
     if args.extra:
         del d
         for name in ("dsv2-b16-t4096", "mtp-b64-ragged", "gqla-b32-t65536"):
-            i2, d2, ms2, dms2 = time_workload(name, args.steps, args.warmup)
+            i2, d2, ms2, _ = time_workload(name, args.steps, args.warmup,
+                                           flush=not args.no_flush)
+            st2, dm2 = _stats(ms2["step"])[0], _stats(ms2["decode"])[0]
             b2 = i2.total_tokens * i2.cfg.D * 2
-            print(json.dumps({"workload": name, "ms_per_step": ms2, "decode_ms": dms2,
-                              "tokens_per_s": i2.total_tokens / (ms2 * 1e-3),
-                              "decode_GBs": b2 / (dms2 * 1e-3) / 1e9}), file=sys.stderr,
+            print(json.dumps({"workload": name, "path": "absorbed", "ms_per_step": st2,
+                              "decode_ms": dm2,
+                              "kernel_ms": {k: _stats(v)[0] for k, v in ms2.items()},
+                              "tokens_per_s": i2.total_tokens / (st2 * 1e-3),
+                              "decode_GBs": b2 / (dm2 * 1e-3) / 1e9}), file=sys.stderr,
                   flush=True)
             del d2
+        for name in ("gqla-b32-t8192", "gqla-b32-t65536"):
+            print(json.dumps(time_gqa_path(name, args.steps, args.warmup,
+                                           flush=not args.no_flush)),
+                  file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":

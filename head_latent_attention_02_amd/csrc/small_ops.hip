@@ -18,46 +18,101 @@ namespace {
 
 constexpr int kQB = 8;  // queries per block in a1 / a4
 
+// 8 consecutive elements as floats (one 16-byte load for bf16, two for fp32)
+__device__ __forceinline__ void load8(const bf16_t* p, float (&x)[8]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
 // ---------------------------------------------------------------- a1 absorb
-// Block (head h, 8 queries).  The queries' no-position parts sit in LDS as fp32; each
-// thread owns latent columns c (coalesced reads of W_UK[w] rows) and keeps 8 sums.
+// Block (head h, 256 latent columns, 8 queries), 256 threads.  Thread (rs, cl) = (tid / 32,
+// tid % 32) owns columns c0 + 8 cl .. +8 and weight rows rs, rs + 8, ...: each W_UK row
+// chunk is one 512-byte coalesced read per 32 lanes, and every weight byte of the block
+// is read once.
+constexpr int kAbsCols = 256;
 template <typename T>
 __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
                                                        const T* __restrict__ w_uk,
                                                        T* __restrict__ q_abs, int NQ, int H,
                                                        int Hw, int d_n, int d_r, int d_c) {
-  extern __shared__ float qs[];  // [kQB][d_n]
-  const int h = blockIdx.x, q0 = blockIdx.y * kQB;
+  extern __shared__ float smem[];
+  float* qs = smem;                       // [kQB][d_n]
+  float* red = smem + kQB * d_n;          // [4 waves][kQB][kAbsCols]
+  const int h = blockIdx.x, c0 = blockIdx.y * kAbsCols, q0 = blockIdx.z * kQB;
   const int w = h / (H / Hw);
   const int nq = min(kQB, NQ - q0);
   const int dq = d_n + d_r, D = d_c + d_r;
-  for (int idx = threadIdx.x; idx < kQB * d_n; idx += blockDim.x) {
+  const int tid = threadIdx.x, rs = tid >> 5, cl = tid & 31;
+  for (int idx = tid; idx < kQB * d_n; idx += blockDim.x) {
     const int jq = idx / d_n, i = idx - jq * d_n;
     qs[idx] = (jq < nq) ? ldf(q + (static_cast<size_t>(q0 + jq) * H + h) * dq + i) : 0.f;
   }
   __syncthreads();
-  const T* W = w_uk + static_cast<size_t>(w) * d_n * d_c;
-  for (int c = threadIdx.x; c < d_c; c += blockDim.x) {
-    float acc[kQB];
+  const int c = c0 + 8 * cl;
+  float acc[kQB][8];
 #pragma unroll
-    for (int jq = 0; jq < kQB; ++jq) acc[jq] = 0.f;
-    for (int i = 0; i < d_n; ++i) {
-      const float wv = ldf(W + static_cast<size_t>(i) * d_c + c);
+  for (int jq = 0; jq < kQB; ++jq)
 #pragma unroll
-      for (int jq = 0; jq < kQB; ++jq) acc[jq] += qs[jq * d_n + i] * wv;
+    for (int e = 0; e < 8; ++e) acc[jq][e] = 0.f;
+  if (c < d_c) {
+    const T* W = w_uk + static_cast<size_t>(w) * d_n * d_c + c;
+#pragma unroll 4
+    for (int i = rs; i < d_n; i += 8) {
+      float wv[8];
+      load8(W + static_cast<size_t>(i) * d_c, wv);
+#pragma unroll
+      for (int jq = 0; jq < kQB; ++jq) {
+        const float qv = qs[jq * d_n + i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[jq][e] = fmaf(qv, wv[e], acc[jq][e]);
+      }
     }
-    for (int jq = 0; jq < nq; ++jq)
-      stf(q_abs + (static_cast<size_t>(q0 + jq) * H + h) * D + c, acc[jq]);
   }
-  for (int idx = threadIdx.x; idx < nq * d_r; idx += blockDim.x) {
-    const int jq = idx / d_r, r = idx - jq * d_r;
-    const size_t qrow = static_cast<size_t>(q0 + jq) * H + h;
-    q_abs[qrow * D + d_c + r] = q[qrow * dq + d_n + r];
+  // the two row slices of a wave (lane halves) meet by a shuffle, the 4 waves in LDS
+#pragma unroll
+  for (int jq = 0; jq < kQB; ++jq)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[jq][e] += __shfl_xor(acc[jq][e], 32, 64);
+  if ((rs & 1) == 0) {
+#pragma unroll
+    for (int jq = 0; jq < kQB; ++jq)
+#pragma unroll
+      for (int e = 0; e < 8; e += 4)
+        *reinterpret_cast<float4*>(&red[((rs >> 1) * kQB + jq) * kAbsCols + 8 * cl + e]) =
+            make_float4(acc[jq][e], acc[jq][e + 1], acc[jq][e + 2], acc[jq][e + 3]);
+  }
+  __syncthreads();
+  for (int idx = tid; idx < kQB * kAbsCols; idx += blockDim.x) {
+    const int jq = idx / kAbsCols, cc = idx - jq * kAbsCols;
+    if (jq >= nq || c0 + cc >= d_c) continue;
+    float v = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v += red[(r * kQB + jq) * kAbsCols + cc];
+    stf(q_abs + (static_cast<size_t>(q0 + jq) * H + h) * D + c0 + cc, v);
+  }
+  if (blockIdx.y == 0) {
+    for (int idx = tid; idx < nq * d_r; idx += blockDim.x) {
+      const int jq = idx / d_r, r = idx - jq * d_r;
+      const size_t qrow = static_cast<size_t>(q0 + jq) * H + h;
+      q_abs[qrow * D + d_c + r] = q[qrow * dq + d_n + r];
+    }
   }
 }
 
 // ---------------------------------------------------------------- a3 combine
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
+// Block per query row, 128 threads, 4 consecutive columns per thread per pass.
+__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       float* __restrict__ o,
                                                       float* __restrict__ lse, int S,
@@ -71,48 +126,86 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (threadIdx.x == 0 && lse) lse[row] = -INFINITY;
     return;
   }
+  const float ml = m * kLog2e;
   float tot = 0.f;
-  for (int u = 0; u < S; ++u) tot += exp2f((lp[u] - m) * kLog2e);
+  for (int u = 0; u < S; ++u) tot += exp2f(fmaf(lp[u], kLog2e, -ml));
   const float inv = 1.f / tot;
-  for (int c = threadIdx.x; c < width; c += blockDim.x) {
-    float acc = 0.f;
+  const float* op = o_part + row * S * width;
+  for (int c = 4 * threadIdx.x; c < width; c += 4 * blockDim.x) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
     for (int u = 0; u < S; ++u) {
-      const float wgt = exp2f((lp[u] - m) * kLog2e);
-      if (wgt > 0.f) acc += wgt * o_part[(row * S + u) * width + c];
+      const float wgt = exp2f(fmaf(lp[u], kLog2e, -ml));
+      if (wgt > 0.f) {   // an empty split (lse -inf) may hold anything
+        const float4 v = *reinterpret_cast<const float4*>(op + static_cast<size_t>(u) * width + c);
+        acc.x = fmaf(wgt, v.x, acc.x);
+        acc.y = fmaf(wgt, v.y, acc.y);
+        acc.z = fmaf(wgt, v.z, acc.z);
+        acc.w = fmaf(wgt, v.w, acc.w);
+      }
     }
-    o[row * width + c] = acc * inv;
+    *reinterpret_cast<float4*>(o + row * width + c) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
   if (threadIdx.x == 0 && lse) lse[row] = m + logf(tot);
 }
 
 // ---------------------------------------------------------------- a4 out_uv
-// Block (head h, 8 queries): the queries' latent outputs sit in LDS; each thread owns
-// value columns v and walks its W_UV row.
+// Block (head h, 32 value rows, 8 queries), 256 threads.  Within a wave, lanes 8r..8r+7
+// read W_UV row v0 + 8 wave + r in 128-byte segments (8 elements a lane); the queries'
+// latent outputs sit in LDS.  The 8 lanes of a row meet by shuffles.
+constexpr int kUvRows = 32;
 template <typename T>
 __global__ __launch_bounds__(256) void out_uv_kernel(const float* __restrict__ o_lat,
                                                      const T* __restrict__ w_uv,
                                                      float* __restrict__ out, int NQ, int H,
                                                      int Hw, int d_c, int d_v) {
   extern __shared__ float os[];  // [kQB][d_c]
-  const int h = blockIdx.x, q0 = blockIdx.y * kQB;
+  const int h = blockIdx.x, v0 = blockIdx.y * kUvRows, q0 = blockIdx.z * kQB;
   const int w = h / (H / Hw);
   const int nq = min(kQB, NQ - q0);
-  for (int idx = threadIdx.x; idx < kQB * d_c; idx += blockDim.x) {
+  const int tid = threadIdx.x;
+  for (int idx = 4 * tid; idx < kQB * d_c; idx += 4 * blockDim.x) {
     const int jq = idx / d_c, c = idx - jq * d_c;
-    os[idx] = (jq < nq) ? o_lat[(static_cast<size_t>(q0 + jq) * H + h) * d_c + c] : 0.f;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (jq < nq)
+      v = *reinterpret_cast<const float4*>(o_lat + (static_cast<size_t>(q0 + jq) * H + h) * d_c + c);
+    *reinterpret_cast<float4*>(&os[idx]) = v;
   }
   __syncthreads();
-  const T* W = w_uv + static_cast<size_t>(w) * d_v * d_c;
-  for (int v = threadIdx.x; v < d_v; v += blockDim.x) {
-    float acc[kQB];
+  const int lane = tid & 63, wave = tid >> 6;
+  const int v = v0 + 8 * wave + (lane >> 3), cg = lane & 7;
+  float acc[kQB];
 #pragma unroll
-    for (int jq = 0; jq < kQB; ++jq) acc[jq] = 0.f;
-    const T* wr = W + static_cast<size_t>(v) * d_c;
-    for (int c = 0; c < d_c; ++c) {
-      const float wv = ldf(wr + c);
+  for (int jq = 0; jq < kQB; ++jq) acc[jq] = 0.f;
+  if (v < d_v) {
+    const T* wr = w_uv + (static_cast<size_t>(w) * d_v + v) * d_c;
+#pragma unroll 2
+    for (int c = 8 * cg; c < d_c; c += 64) {
+      float wv[8];
+      load8(wr + c, wv);
 #pragma unroll
-      for (int jq = 0; jq < kQB; ++jq) acc[jq] += os[jq * d_c + c] * wv;
+      for (int jq = 0; jq < kQB; ++jq) {
+        const float4 a = *reinterpret_cast<const float4*>(&os[jq * d_c + c]);
+        const float4 b = *reinterpret_cast<const float4*>(&os[jq * d_c + c + 4]);
+        float t = acc[jq];
+        t = fmaf(a.x, wv[0], t); t = fmaf(a.y, wv[1], t);
+        t = fmaf(a.z, wv[2], t); t = fmaf(a.w, wv[3], t);
+        t = fmaf(b.x, wv[4], t); t = fmaf(b.y, wv[5], t);
+        t = fmaf(b.z, wv[6], t); t = fmaf(b.w, wv[7], t);
+        acc[jq] = t;
+      }
     }
+  }
+#pragma unroll
+  for (int jq = 0; jq < kQB; ++jq) {
+    float t = acc[jq];
+    t += __shfl_xor(t, 1, 64);
+    t += __shfl_xor(t, 2, 64);
+    t += __shfl_xor(t, 4, 64);
+    acc[jq] = t;
+  }
+  if (v < d_v && cg == 0) {
     for (int jq = 0; jq < nq; ++jq) out[(static_cast<size_t>(q0 + jq) * H + h) * d_v + v] = acc[jq];
   }
 }
@@ -201,8 +294,8 @@ __global__ __launch_bounds__(256) void expand_kernel(const T* __restrict__ pool,
 hipError_t launch_absorb_q(const mla_shape_t& s, const void* q, const void* w_uk,
                            void* q_abs, hipStream_t st) {
   const int NQ = s.batch * s.s_q;
-  dim3 grid(s.n_heads, (NQ + kQB - 1) / kQB);
-  const size_t lds = sizeof(float) * kQB * s.d_nope;
+  dim3 grid(s.n_heads, (s.d_c + kAbsCols - 1) / kAbsCols, (NQ + kQB - 1) / kQB);
+  const size_t lds = sizeof(float) * kQB * (s.d_nope + 4 * kAbsCols);
   if (s.dtype == MLA_F32)
     hipLaunchKernelGGL(absorb_q_kernel<float>, grid, dim3(256), lds, st,
                        static_cast<const float*>(q), static_cast<const float*>(w_uk),
@@ -227,14 +320,14 @@ hipError_t launch_combine(const mla_shape_t& s, int width, const float* o_part,
 hipError_t launch_out_uv(const mla_shape_t& s, const float* o_lat, const void* w_uv,
                          float* out, hipStream_t st) {
   const int NQ = s.batch * s.s_q;
-  dim3 grid(s.n_heads, (NQ + kQB - 1) / kQB);
+  dim3 grid(s.n_heads, (s.d_v + kUvRows - 1) / kUvRows, (NQ + kQB - 1) / kQB);
   const size_t lds = sizeof(float) * kQB * s.d_c;
   if (s.dtype == MLA_F32)
-    hipLaunchKernelGGL(out_uv_kernel<float>, grid, dim3(128), lds, st, o_lat,
+    hipLaunchKernelGGL(out_uv_kernel<float>, grid, dim3(256), lds, st, o_lat,
                        static_cast<const float*>(w_uv), out, NQ, s.n_heads, s.n_wheads,
                        s.d_c, s.d_v);
   else
-    hipLaunchKernelGGL(out_uv_kernel<bf16_t>, grid, dim3(128), lds, st, o_lat,
+    hipLaunchKernelGGL(out_uv_kernel<bf16_t>, grid, dim3(256), lds, st, o_lat,
                        static_cast<const bf16_t*>(w_uv), out, NQ, s.n_heads, s.n_wheads,
                        s.d_c, s.d_v);
   return hipGetLastError();
