@@ -1,12 +1,322 @@
-// Matrix-core (MFMA) GQA-path decode: not built yet; every shape takes the generic path.
+// Matrix-core (MFMA) GQA-path decode over the expanded per-group cache, bf16, with
+// d_nope = d_v = 128, d_rope = 64, page 64 and at most 16 query rows per group.
+//
+// What it computes: for query row (s, h) of group j = w(h) and chunk u, the split-KV
+// partials of softmax attention with keys [K_j[t] ; k^R[t]] and values V_j[t] over the
+// chunk's visible tokens (AI Radio episode on GQLA, "Key concepts": the GQA path keeps
+// per-group keys and values, the RoPE key is shared; "How to upgrade GQA models to
+// MLA...", Under the hood: both paths give the same attention).
+//
+// The path streams 4224 bytes per token (8 groups x 256 B of K and V, plus 128 B of
+// k^R) for 20 KFLOP, so it is bound by HBM and every design choice serves streaming:
+//  * One workgroup = one (sequence b, chunk u, group j); its 4 waves take the chunk's
+//    32-token tiles round robin, each with a private online softmax, and merge at the
+//    end through LDS.  No barrier inside the loop.
+//  * Keys go from HBM straight into A-operand registers of v_mfma_f32_32x32x16_bf16
+//    (token = M, query row = N).  The contraction index is permuted so that every lane
+//    reads 128 contiguous bytes of its token's K_j row and 64 of its k^R row; the query
+//    operand uses the same permutation, which leaves the dot products unchanged.
+//  * The next tile's 20 loads per lane are in flight while the current tile computes
+//    (two register tiles, ping-pong, loads always issued so the wait counts stay exact).
+//  * Values pass through a wave-private 8 KB LDS tile (16-byte chunks XOR-swizzled per
+//    token) and are read back transposed with ds_read_b64_tr_b16 as the A operand of
+//    O^T += V^T P^T.  P comes straight from the score accumulators: the token order of
+//    the value product is permuted to match the score layout, so P never leaves the
+//    lane that computed it.
+//  * Workgroups of one (b, u) sit 8 apart in the grid so that all groups of a chunk run
+//    on one XCD and share its L2 for the k^R rows.
+// Rows past the chunk end are loaded from the tile's first token (valid data) and
+// masked, so NaN padding in a last page never reaches an MFMA.
+#include <math.h>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mla {
-bool gqa_decode_mfma_supported(const mla_shape_t&) { return false; }
-hipError_t launch_gqa_decode_mfma(const mla_shape_t&, const void*, const void*, const void*,
-                                  const void*, const int32_t*, const int32_t*, float*, float*,
-                                  hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kDN = 128;            // no-position key width
+constexpr int kDV = 128;            // value width
+constexpr int kDR = 64;             // RoPE key width
+constexpr int kPage = 64;
+constexpr int kTT = 32;             // tokens per tile
+constexpr int kKN = kDN / 16;       // 8 K-steps over K_j
+constexpr int kKR = kDR / 16;       // 4 K-steps over k^R
+constexpr int kWaves = 4;
+constexpr int kMaxRows = 16;        // query rows per group (s_q * H / G)
+constexpr int kVRowB = kDV * 2;     // 256-byte value rows in LDS
+constexpr int kVTileB = kTT * kVRowB;
+
+struct Tile {
+  bf16x8 k[kKN];   // K-step ks: K_j[token][64 g + 8 ks, +8)
+  bf16x8 r[kKR];   // K-step kKN + ks: k^R[token][32 g + 8 ks, +8)
+  u32x4 v[8];      // load i: V_j[4 i + lane / 16][8 (lane % 16), +8)
+};
+
+struct Args {
+  const bf16_t* k;
+  const bf16_t* v;
+  const bf16_t* kr;
+  const int32_t* ptb;   // page-table row of sequence b
+  int G, j, lo, hi;
+};
+
+struct Smem {
+  union {
+    char vtile[kWaves][kVTileB];                // per-wave value tile
+    float red_o[kWaves][kMaxRows][kDV];         // per-wave O, after the loop
+  };
+  float red_m[kWaves][32];
+  float red_l[kWaves][32];
+};
+
+__device__ __forceinline__ int vswz(int tok) { return 2 * (tok & 3); }
+
+__device__ __forceinline__ bf16x8 ld_stream(const bf16_t* p) {
+  return __builtin_bit_cast(bf16x8,
+                            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
 }
+
+__device__ __forceinline__ void load_tile(Tile& tl, const Args& a, int t0, int lane) {
+  const int page = a.ptb[t0 >> 6];
+  const size_t slot0 = static_cast<size_t>(page) * kPage + (t0 & (kPage - 1));
+  const int valid = a.hi - t0;
+  const int m = lane & 31, g = lane >> 5;
+  const size_t sk = slot0 + ((m < valid) ? m : 0);
+  const bf16_t* kp = a.k + (sk * a.G + a.j) * kDN + 64 * g;
+#pragma unroll
+  for (int ks = 0; ks < kKN; ++ks) tl.k[ks] = ld_stream(kp + 8 * ks);
+  const bf16_t* rp = a.kr + sk * kDR + 32 * g;
+#pragma unroll
+  for (int ks = 0; ks < kKR; ++ks) tl.r[ks] = *reinterpret_cast<const bf16x8*>(rp + 8 * ks);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int tv = 4 * i + (lane >> 4);
+    const size_t sv = slot0 + ((tv < valid) ? tv : 0);
+    tl.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+        a.v + (sv * a.G + a.j) * kDV + 8 * (lane & 15)));
+  }
+}
+
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+struct RowState {
+  float m;   // running maximum (log2 units), -inf before the first visible token
+  float l;   // this lane's share of the running sum
+};
+
+// One tile: scores, online softmax, value product.  vl = visible tokens of this lane's
+// row in the tile (tokens 0 .. vl-1).
+__device__ __forceinline__ void process_tile(const Tile& tl, const bf16x8 (&qn)[kKN],
+                                             const bf16x8 (&qr)[kKR], char* vt,
+                                             const int (&rdo)[2][2], int vl, float zscale,
+                                             int lane, RowState& st, f32x16 (&acc)[4]) {
+  const int g = lane >> 5;
+  // value tile into the wave's LDS slot (swizzled 16-byte chunks)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int tv = 4 * i + (lane >> 4);
+    *reinterpret_cast<u32x4*>(vt + tv * kVRowB + (((lane & 15) ^ vswz(tv)) * 16)) = tl.v[i];
+  }
+  f32x16 s = {};
+#pragma unroll
+  for (int ks = 0; ks < kKN; ++ks)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.k[ks], qn[ks], s, 0, 0, 0);
+#pragma unroll
+  for (int ks = 0; ks < kKR; ++ks)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.r[ks], qr[ks], s, 0, 0, 0);
+  // lane (row n, half g) holds tokens 8 (jj / 4) + 4 g + jj % 4
+  float mx = -INFINITY;
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj)
+    if (8 * (jj >> 2) + 4 * g + (jj & 3) < vl) mx = fmaxf(mx, s[jj]);
+  mx = xhalf_max(mx * zscale);
+  const float m_new = fmaxf(st.m, mx);
+  if (__builtin_amdgcn_ballot_w64(m_new > st.m)) {
+    const float alpha = (st.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mb][e] *= alpha;
+    st.m = m_new;
+  }
+  const bool live = st.m != -INFINITY;
+  bf16x8 pb[2];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const bool vis = live && (8 * (jj >> 2) + 4 * g + (jj & 3) < vl);
+    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[jj], zscale, -st.m)) : 0.f;
+    st.l += p;
+    pb[jj >> 3][jj & 7] = static_cast<__bf16>(p);
+  }
+  // O^T[col][row] += V^T P^T over the tile's 32 tokens, in the score layout's order
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int cofs = 64 * mb;   // 32 columns = 4 chunks of 16 bytes
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(__attribute__((address_space(3))) char*)(vt + (rdo[kt][0] ^ cofs)));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(__attribute__((address_space(3))) char*)(vt + (rdo[kt][1] ^ cofs)));
+      const bf16x8 av = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kt], acc[mb], 0, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(256, 1) void gqa_decode_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kpool,
+    const bf16_t* __restrict__ vpool, const bf16_t* __restrict__ krpool,
+    const int32_t* __restrict__ pt, const int32_t* __restrict__ lens,
+    float* __restrict__ o_part, float* __restrict__ lse_part, int s_q, int H, int G,
+    int max_pages, int S, int split_tokens, float zscale, int n_units) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  const int wg = blockIdx.x;
+  const int rest = wg >> 3;
+  const int j = rest % G;
+  const int unit = (rest / G) * 8 + (wg & 7);
+  if (unit >= n_units) return;   // uniform for the workgroup, before any barrier
+  const int b = unit / S, u = unit - b * S;
+  const int T = lens[b];
+  Args a;
+  a.k = kpool;
+  a.v = vpool;
+  a.kr = krpool;
+  a.ptb = pt + static_cast<size_t>(b) * max_pages;
+  a.G = G;
+  a.j = j;
+  split_range(T, u, S, kPage, split_tokens, a.lo, a.hi);
+  const int n_tiles = (a.hi > a.lo) ? (a.hi - a.lo + kTT - 1) / kTT : 0;
+  const int hg = H / G, R = s_q * hg;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 31, g = lane >> 5;
+
+  // query operand: row n = (s, hh), same contraction permutation as the keys
+  bf16x8 qn[kKN], qr[kKR];
+  int row_lim = 0;   // exclusive token bound of this lane's row
+  {
+    const int r = (n < R) ? n : 0;
+    const int s = r / hg, h = j * hg + (r - s * hg);
+    const bf16_t* qp = q + ((static_cast<size_t>(b) * s_q + s) * H + h) * (kDN + kDR);
+    const bf16x8 zero = {};
+#pragma unroll
+    for (int ks = 0; ks < kKN; ++ks)
+      qn[ks] = (n < R) ? *reinterpret_cast<const bf16x8*>(qp + 64 * g + 8 * ks) : zero;
+#pragma unroll
+    for (int ks = 0; ks < kKR; ++ks)
+      qr[ks] = (n < R) ? *reinterpret_cast<const bf16x8*>(qp + kDN + 32 * g + 8 * ks) : zero;
+    row_lim = min(a.hi, T - s_q + s + 1);
+  }
+  // transposed-read byte offsets (column block 0) for the two halves of each K-step
+  int rdo[2][2];
+  {
+    const int q16 = lane >> 4, L = lane & 15;
+    const int mh = q16 & 1, gg = q16 >> 1;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int tok = 16 * kt + 8 * hf + 4 * gg + (L >> 2);
+        const int c16 = 2 * mh + ((L & 3) >> 1);
+        rdo[kt][hf] = tok * kVRowB + ((c16 ^ vswz(tok)) * 16) + 8 * (L & 1);
+      }
+  }
+  // column block mb adds 4 mb to the chunk index (whose block-0 value is below 4), so
+  // the swizzled byte offset of block mb is rdo ^ (64 mb)
+  char* vt = &sm.vtile[wave][0];
+
+  RowState st = {-INFINITY, 0.f};
+  f32x16 acc[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x16{};
+
+  if (wave < n_tiles) {
+    Tile A, B;
+    load_tile(A, a, a.lo + wave * kTT, lane);
+    for (int k = wave;; k += 2 * kWaves) {
+      load_tile(B, a, a.lo + min(k + kWaves, n_tiles - 1) * kTT, lane);
+      process_tile(A, qn, qr, vt, rdo, row_lim - (a.lo + k * kTT), zscale, lane, st, acc);
+      if (k + kWaves >= n_tiles) break;
+      load_tile(A, a, a.lo + min(k + 2 * kWaves, n_tiles - 1) * kTT, lane);
+      process_tile(B, qn, qr, vt, rdo, row_lim - (a.lo + (k + kWaves) * kTT), zscale, lane,
+                   st, acc);
+      if (k + 2 * kWaves >= n_tiles) break;
+    }
+  }
+
+  // merge the 4 waves: each writes its state into its own (now free) value tile
+  const float l_tot = xhalf_sum(st.l);
+  if (g == 0) {
+    sm.red_m[wave][n] = st.m;
+    sm.red_l[wave][n] = l_tot;
+  }
+  if (n < R) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        sm.red_o[wave][n][32 * mb + 8 * (e >> 2) + 4 * g + (e & 3)] = acc[mb][e];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < R * kDV; idx += blockDim.x) {
+    const int r = idx / kDV, c = idx - r * kDV;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.red_m[w][r]);
+    float o = 0.f, lsum = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm.red_m[w][r];
+        const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+        lsum += f * sm.red_l[w][r];
+        o += f * sm.red_o[w][r][c];
+      }
+    }
+    const int s = r / hg, h = j * hg + (r - s * hg);
+    const size_t orow = ((static_cast<size_t>(b) * s_q + s) * H + h) * S + u;
+    o_part[orow * kDV + c] = (lsum > 0.f) ? o / lsum : 0.f;
+    if (c == 0) lse_part[orow] = (lsum > 0.f) ? (M + log2f(lsum)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace
+
+bool gqa_decode_mfma_supported(const mla_shape_t& s) {
+  return s.dtype == MLA_BF16 && s.d_nope == kDN && s.d_v == kDV && s.d_rope == kDR &&
+         s.page_size == kPage && s.s_q * (s.n_heads / s.n_wheads) <= kMaxRows;
+}
+
+hipError_t launch_gqa_decode_mfma(const mla_shape_t& s, const void* q, const void* k,
+                                  const void* v, const void* kr, const int32_t* pt,
+                                  const int32_t* lens, float* o_part, float* lse_part,
+                                  hipStream_t st) {
+  const int n_units = s.batch * s.n_splits;
+  const unsigned grid = static_cast<unsigned>((n_units + 7) / 8) * 8u * s.n_wheads;
+  hipLaunchKernelGGL(gqa_decode_mfma_kernel, dim3(grid), dim3(256), 0, st,
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                     static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(kr), pt, lens,
+                     o_part, lse_part, s.s_q, s.n_heads, s.n_wheads, s.max_pages,
+                     s.n_splits, s.split_tokens, s.softmax_scale * kLog2e, n_units);
+  return hipGetLastError();
+}
+
 }  // namespace mla

@@ -67,7 +67,8 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
     for (int e = 0; e < 8; ++e) acc[jq][e] = 0.f;
   if (c < d_c) {
     const T* W = w_uk + static_cast<size_t>(w) * d_n * d_c + c;
-#pragma unroll 4
+    // all of a thread's weight loads are issued back to back (16 in flight at d_n = 128)
+#pragma unroll 16
     for (int i = rs; i < d_n; i += 8) {
       float wv[8];
       load8(W + static_cast<size_t>(i) * d_c, wv);
@@ -133,16 +134,17 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   const float* op = o_part + row * S * width;
   for (int c = 4 * threadIdx.x; c < width; c += 4 * blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
+    // loads are unconditional so that 16 of them can be in flight; an empty split
+    // (lse -inf, weight 0) may hold anything, so its values are selected away, not scaled
+#pragma unroll 16
     for (int u = 0; u < S; ++u) {
       const float wgt = exp2f(fmaf(lp[u], kLog2e, -ml));
-      if (wgt > 0.f) {   // an empty split (lse -inf) may hold anything
-        const float4 v = *reinterpret_cast<const float4*>(op + static_cast<size_t>(u) * width + c);
-        acc.x = fmaf(wgt, v.x, acc.x);
-        acc.y = fmaf(wgt, v.y, acc.y);
-        acc.z = fmaf(wgt, v.z, acc.z);
-        acc.w = fmaf(wgt, v.w, acc.w);
-      }
+      const float4 v = *reinterpret_cast<const float4*>(op + static_cast<size_t>(u) * width + c);
+      const bool use = wgt > 0.f;
+      acc.x = fmaf(wgt, use ? v.x : 0.f, acc.x);
+      acc.y = fmaf(wgt, use ? v.y : 0.f, acc.y);
+      acc.z = fmaf(wgt, use ? v.z : 0.f, acc.z);
+      acc.w = fmaf(wgt, use ? v.w : 0.f, acc.w);
     }
     *reinterpret_cast<float4*>(o + row * width + c) =
         make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(256) void out_uv_kernel(const float* __restrict__ o
   for (int jq = 0; jq < kQB; ++jq) acc[jq] = 0.f;
   if (v < d_v) {
     const T* wr = w_uv + (static_cast<size_t>(w) * d_v + v) * d_c;
-#pragma unroll 2
+#pragma unroll 8
     for (int c = 8 * cg; c < d_c; c += 64) {
       float wv[8];
       load8(wr + c, wv);

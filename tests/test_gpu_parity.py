@@ -202,7 +202,8 @@ def expanded_pools(d):
 
 
 @pytest.mark.parametrize("dtype,ctx,S", [("f32", [300, 64, 1], 3), ("bf16", [1000, 129], 2),
-                                         ("bf16", [4096, 2000], 4)])
+                                         ("bf16", [4096, 2000], 4),
+                                         ("bf16", [1, 33, 64, 65, 95], 8)])
 def test_gqla_expand_and_gqa_path(dtype, ctx, S):
     if dtype == "f32":
         cfg = Config("gqla-tiny-f32", "f32", len(ctx), 1, 8, 2, 64, 16, 32, 32,
@@ -234,6 +235,13 @@ def test_gqla_expand_and_gqa_path(dtype, ctx, S):
     announce(f"  gqa errors out={e_out:.3e} lse={e_lse:.3e} "
              f"kind={mla.gqla_decode_kernel_kind(d.shape)}")
     assert e_out <= tol and e_lse <= tol
+
+
+def test_gqa_path_uses_matrix_cores_at_gqla_shapes():
+    for sq in (1, 2):
+        cfg = get_config("gqla-b32-t8192", s_q=sq)
+        d = DeviceInputs(make_inputs(cfg.with_(batch=1, ctx=("list", [64]))))
+        assert mla.gqla_decode_kernel_kind(d.shape) == 1
 
 
 def test_gqa_decode_on_oracle_expanded_cache():
@@ -287,6 +295,29 @@ def test_full_long_b4_t131072():
 
 def test_full_mtp_b64_ragged():
     sampled_full_check(get_config("mtp-b64-ragged"), [0, 17, 40, 63], [0, 127, 77])
+
+
+def test_full_gqla_b32_t65536_gqa_path():
+    """GQA path at its largest size: 32 sequences of 65536 tokens, expanded on the GPU."""
+    cfg = get_config("gqla-b32-t65536")
+    inp = make_inputs(cfg)
+    announce(f"case full gqa {cfg.name} tokens={inp.total_tokens} S={cfg.n_splits}")
+    d = DeviceInputs(inp)
+    assert mla.gqla_decode_kernel_kind(d.shape) == 1
+    k, v, kr = expanded_pools(d)
+    mla.gqla_expand_cache(d.shape, d.pool, d.w_uk, d.w_uv, k, v, kr)
+    gqa_step(d, k, v, kr)
+    got, got_lse = d.out.cpu().numpy(), d.lse.cpu().numpy()
+    del d, k, v, kr
+    torch.cuda.empty_cache()
+    batches, heads = [0, 13, 31], list(range(cfg.n_heads))
+    want, lse = ref.mla_decode_naive(inp.q, inp.pool_view(), inp.page_table, inp.ctx_lens,
+                                     inp.w_uk, inp.w_uv, cfg.scale, cfg.page_size, cfg.d_c,
+                                     batches=batches, heads=heads)
+    sel = np.ix_(batches, range(cfg.s_q), heads)
+    e, el = rel_err(got[sel], want[sel]), rel_err(got_lse[sel], lse[sel])
+    announce(f"  sampled errors out={e:.3e} lse={el:.3e}")
+    assert e <= TOL["bf16"] and el <= TOL["bf16"]
 
 
 # ------------------------------------------- reference moves (online-softmax fold path)
