@@ -12,17 +12,16 @@
 //  * One workgroup = one (sequence b, chunk u, group j); its 4 waves take the chunk's
 //    32-token tiles round robin, each with a private online softmax, and merge at the
 //    end through LDS.  No barrier inside the loop.
-//  * Keys go from HBM straight into A-operand registers of v_mfma_f32_32x32x16_bf16
-//    (token = M, query row = N).  The contraction index is permuted so that every lane
-//    reads 128 contiguous bytes of its token's K_j row and 64 of its k^R row; the query
-//    operand uses the same permutation, which leaves the dot products unchanged.
+//  * Every load instruction reads whole rows: 16 lanes per 256-byte K_j or V_j row, 8
+//    lanes per 128-byte k^R row, so each touches only full cache lines.  The rows go
+//    through a wave-private 20 KB LDS tile (16-byte chunks XOR-swizzled per token) that
+//    re-lays them out for v_mfma_f32_32x32x16_bf16: keys as the A operand of
+//    S^T = K Q^T (token = M, query row = N), values read back transposed with
+//    ds_read_b64_tr_b16 as the A operand of O^T += V^T P^T.  P comes straight from the
+//    score accumulators: the token order of the value product is permuted to match the
+//    score layout, so P never leaves the lane that computed it.
 //  * The next tile's 20 loads per lane are in flight while the current tile computes
 //    (two register tiles, ping-pong, loads always issued so the wait counts stay exact).
-//  * Values pass through a wave-private 8 KB LDS tile (16-byte chunks XOR-swizzled per
-//    token) and are read back transposed with ds_read_b64_tr_b16 as the A operand of
-//    O^T += V^T P^T.  P comes straight from the score accumulators: the token order of
-//    the value product is permuted to match the score layout, so P never leaves the
-//    lane that computed it.
 //  * Workgroups of one (b, u) sit 8 apart in the grid so that all groups of a chunk run
 //    on one XCD and share its L2 for the k^R rows.
 // Rows past the chunk end are loaded from the tile's first token (valid data) and
@@ -51,12 +50,21 @@ constexpr int kKR = kDR / 16;       // 4 K-steps over k^R
 constexpr int kWaves = 4;
 constexpr int kMaxRows = 16;        // query rows per group (s_q * H / G)
 constexpr int kVRowB = kDV * 2;     // 256-byte value rows in LDS
-constexpr int kVTileB = kTT * kVRowB;
 
+constexpr int kKRowB = kDN * 2;     // 256-byte key rows
+constexpr int kRRowB = kDR * 2;     // 128-byte RoPE-key rows
+
+// One tile's rows in registers on their way to LDS (16 bytes per lane and load).
 struct Tile {
-  bf16x8 k[kKN];   // K-step ks: K_j[token][64 g + 8 ks, +8)
-  bf16x8 r[kKR];   // K-step kKN + ks: k^R[token][32 g + 8 ks, +8)
+  u32x4 k[8];      // load i: K_j[4 i + lane / 16][8 (lane % 16), +8)
+  u32x4 r[4];      // load i: k^R[8 i + lane / 8][8 (lane % 8), +8)
   u32x4 v[8];      // load i: V_j[4 i + lane / 16][8 (lane % 16), +8)
+};
+
+struct WaveTile {
+  char k[kTT * kKRowB];
+  char r[kTT * kRRowB];
+  char v[kTT * kVRowB];
 };
 
 struct Args {
@@ -69,38 +77,39 @@ struct Args {
 
 struct Smem {
   union {
-    char vtile[kWaves][kVTileB];                // per-wave value tile
+    WaveTile tile[kWaves];                      // per-wave row tiles
     float red_o[kWaves][kMaxRows][kDV];         // per-wave O, after the loop
   };
   float red_m[kWaves][32];
   float red_l[kWaves][32];
 };
 
+// chunk swizzles: keys and RoPE keys are read 16 tokens x one chunk at a time, values
+// 4 tokens x two chunks at a time (transposed)
+__device__ __forceinline__ int kswz(int tok) { return tok & 15; }
+__device__ __forceinline__ int rswz(int tok) { return tok & 7; }
 __device__ __forceinline__ int vswz(int tok) { return 2 * (tok & 3); }
 
-__device__ __forceinline__ bf16x8 ld_stream(const bf16_t* p) {
-  return __builtin_bit_cast(bf16x8,
-                            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+__device__ __forceinline__ u32x4 ld_stream(const bf16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
 __device__ __forceinline__ void load_tile(Tile& tl, const Args& a, int t0, int lane) {
   const int page = a.ptb[t0 >> 6];
   const size_t slot0 = static_cast<size_t>(page) * kPage + (t0 & (kPage - 1));
   const int valid = a.hi - t0;
-  const int m = lane & 31, g = lane >> 5;
-  const size_t sk = slot0 + ((m < valid) ? m : 0);
-  const bf16_t* kp = a.k + (sk * a.G + a.j) * kDN + 64 * g;
-#pragma unroll
-  for (int ks = 0; ks < kKN; ++ks) tl.k[ks] = ld_stream(kp + 8 * ks);
-  const bf16_t* rp = a.kr + sk * kDR + 32 * g;
-#pragma unroll
-  for (int ks = 0; ks < kKR; ++ks) tl.r[ks] = *reinterpret_cast<const bf16x8*>(rp + 8 * ks);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int tv = 4 * i + (lane >> 4);
-    const size_t sv = slot0 + ((tv < valid) ? tv : 0);
-    tl.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-        a.v + (sv * a.G + a.j) * kDV + 8 * (lane & 15)));
+    const size_t sv = (slot0 + ((tv < valid) ? tv : 0)) * a.G + a.j;
+    tl.k[i] = ld_stream(a.k + sv * kDN + 8 * (lane & 15));
+    tl.v[i] = ld_stream(a.v + sv * kDV + 8 * (lane & 15));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tr = 8 * i + (lane >> 3);
+    const size_t sr = slot0 + ((tr < valid) ? tr : 0);
+    tl.r[i] = *reinterpret_cast<const u32x4*>(a.kr + sr * kDR + 8 * (lane & 7));
   }
 }
 
@@ -124,23 +133,41 @@ struct RowState {
 // One tile: scores, online softmax, value product.  vl = visible tokens of this lane's
 // row in the tile (tokens 0 .. vl-1).
 __device__ __forceinline__ void process_tile(const Tile& tl, const bf16x8 (&qn)[kKN],
-                                             const bf16x8 (&qr)[kKR], char* vt,
+                                             const bf16x8 (&qr)[kKR], WaveTile& wt,
                                              const int (&rdo)[2][2], int vl, float zscale,
                                              int lane, RowState& st, f32x16 (&acc)[4]) {
-  const int g = lane >> 5;
-  // value tile into the wave's LDS slot (swizzled 16-byte chunks)
+  const int g = lane >> 5, m = lane & 31;
+  // rows into the wave's LDS tile (swizzled 16-byte chunks)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int tv = 4 * i + (lane >> 4);
-    *reinterpret_cast<u32x4*>(vt + tv * kVRowB + (((lane & 15) ^ vswz(tv)) * 16)) = tl.v[i];
+    const int t = 4 * i + (lane >> 4), c = lane & 15;
+    *reinterpret_cast<u32x4*>(wt.k + t * kKRowB + ((c ^ kswz(t)) * 16)) = tl.k[i];
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 8 * i + (lane >> 3), c = lane & 7;
+    *reinterpret_cast<u32x4*>(wt.r + t * kRRowB + ((c ^ rswz(t)) * 16)) = tl.r[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = 4 * i + (lane >> 4), c = lane & 15;
+    *reinterpret_cast<u32x4*>(wt.v + t * kVRowB + ((c ^ vswz(t)) * 16)) = tl.v[i];
+  }
+  // S^T = K Q^T: lane (token m, half g) takes chunk 2 ks + g of its key row
   f32x16 s = {};
 #pragma unroll
-  for (int ks = 0; ks < kKN; ++ks)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.k[ks], qn[ks], s, 0, 0, 0);
+  for (int ks = 0; ks < kKN; ++ks) {
+    const bf16x8 ak = *reinterpret_cast<const bf16x8*>(
+        wt.k + m * kKRowB + (((2 * ks + g) ^ kswz(m)) * 16));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qn[ks], s, 0, 0, 0);
+  }
 #pragma unroll
-  for (int ks = 0; ks < kKR; ++ks)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.r[ks], qr[ks], s, 0, 0, 0);
+  for (int ks = 0; ks < kKR; ++ks) {
+    const bf16x8 ar = *reinterpret_cast<const bf16x8*>(
+        wt.r + m * kRRowB + (((2 * ks + g) ^ rswz(m)) * 16));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar, qr[ks], s, 0, 0, 0);
+  }
+  char* vt = wt.v;
   // lane (row n, half g) holds tokens 8 (jj / 4) + 4 g + jj % 4
   float mx = -INFINITY;
 #pragma unroll
@@ -209,7 +236,7 @@ __global__ __launch_bounds__(256, 1) void gqa_decode_mfma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
 
-  // query operand: row n = (s, hh), same contraction permutation as the keys
+  // query operand: row n = (s, hh)
   bf16x8 qn[kKN], qr[kKR];
   int row_lim = 0;   // exclusive token bound of this lane's row
   {
@@ -219,10 +246,10 @@ __global__ __launch_bounds__(256, 1) void gqa_decode_mfma_kernel(
     const bf16x8 zero = {};
 #pragma unroll
     for (int ks = 0; ks < kKN; ++ks)
-      qn[ks] = (n < R) ? *reinterpret_cast<const bf16x8*>(qp + 64 * g + 8 * ks) : zero;
+      qn[ks] = (n < R) ? *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * g) : zero;
 #pragma unroll
     for (int ks = 0; ks < kKR; ++ks)
-      qr[ks] = (n < R) ? *reinterpret_cast<const bf16x8*>(qp + kDN + 32 * g + 8 * ks) : zero;
+      qr[ks] = (n < R) ? *reinterpret_cast<const bf16x8*>(qp + kDN + 16 * ks + 8 * g) : zero;
     row_lim = min(a.hi, T - s_q + s + 1);
   }
   // transposed-read byte offsets (column block 0) for the two halves of each K-step
@@ -241,7 +268,7 @@ __global__ __launch_bounds__(256, 1) void gqa_decode_mfma_kernel(
   }
   // column block mb adds 4 mb to the chunk index (whose block-0 value is below 4), so
   // the swizzled byte offset of block mb is rdo ^ (64 mb)
-  char* vt = &sm.vtile[wave][0];
+  WaveTile& wt = sm.tile[wave];
 
   RowState st = {-INFINITY, 0.f};
   f32x16 acc[4];
@@ -251,18 +278,23 @@ __global__ __launch_bounds__(256, 1) void gqa_decode_mfma_kernel(
   if (wave < n_tiles) {
     Tile A, B;
     load_tile(A, a, a.lo + wave * kTT, lane);
+    // the scheduling barriers keep every load of the next tile ahead of the first use of
+    // the current one, so a whole tile is always in flight
     for (int k = wave;; k += 2 * kWaves) {
       load_tile(B, a, a.lo + min(k + kWaves, n_tiles - 1) * kTT, lane);
-      process_tile(A, qn, qr, vt, rdo, row_lim - (a.lo + k * kTT), zscale, lane, st, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      process_tile(A, qn, qr, wt, rdo, row_lim - (a.lo + k * kTT), zscale, lane, st, acc);
       if (k + kWaves >= n_tiles) break;
       load_tile(A, a, a.lo + min(k + 2 * kWaves, n_tiles - 1) * kTT, lane);
-      process_tile(B, qn, qr, vt, rdo, row_lim - (a.lo + (k + kWaves) * kTT), zscale, lane,
+      __builtin_amdgcn_sched_barrier(0);
+      process_tile(B, qn, qr, wt, rdo, row_lim - (a.lo + (k + kWaves) * kTT), zscale, lane,
                    st, acc);
       if (k + 2 * kWaves >= n_tiles) break;
     }
   }
 
-  // merge the 4 waves: each writes its state into its own (now free) value tile
+  // merge the 4 waves: each writes its O into the LDS the tiles used
+  __syncthreads();
   const float l_tot = xhalf_sum(st.l);
   if (g == 0) {
     sm.red_m[wave][n] = st.m;
