@@ -7,12 +7,18 @@ ABI of libmla.so on one HIP stream.  The workload (default: batch 4 x 131072-tok
 contexts, 128 heads, latent 512 + RoPE 64, bf16, split-KV over 32 chunks) is seeded and
 synthetic and is resident in HBM before timing starts.
 
+Every step is bracketed by HIP events recorded on the launch stream, with events between
+its four kernels; a 1 GiB fill between steps (outside the events) evicts the 256 MB
+last-level cache so every step reads the cache from HBM.  ms_per_step is the median
+step time (p10/p90 beside it).
+
 Prints ONE JSON line.  `value` is cached-latent-tokens/s of the whole step.
 `roofline` describes the decode kernel (the dominant one): algorithmic bytes (every
-cached token's 576 bf16 once) / its average launch time, measured with HIP events on
-the launch stream; `traffic` comes from the committed rocprofv3 counter summary when it
-was taken on the current kernel source, else null.  `cpu_baseline` times the float64
-CPU oracle (naive, non-absorbed MLA) on a bounded sample of the same workload.
+cached token's 576 bf16 once) / its median launch time from those events; `traffic`
+comes from the committed rocprofv3 counter summary when it was taken on the current
+kernel source, else null.  `cpu_baseline` times the float64 CPU oracle (naive,
+non-absorbed MLA) on a bounded sample of the same workload.  `--path gqa` times the
+GQLA per-group path instead (decode + combine on the expanded cache).
 """
 import argparse
 import hashlib
@@ -31,8 +37,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_absorbed_long_b4_t131072_t
 
 
 def kernel_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the decode kernel's source code with comments and blank lines removed, so
+    that a counter summary stays valid across comment-only edits."""
+    code = []
+    with open(KERNEL_SRC) as f:
+        for line in f:
+            line = line.split("//", 1)[0].strip()
+            if line:
+                code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def parse():
@@ -47,6 +60,8 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--extra", action="store_true",
                     help="also time the other workloads (stderr lines)")
+    ap.add_argument("--path", choices=("absorbed", "gqa"), default="absorbed",
+                    help="absorbed MLA step (default) or the GQLA per-group GQA path")
     ap.add_argument("--no-flush", action="store_true",
                     help="do not flush the last-level cache between steps")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -206,10 +221,12 @@ def time_gqa_path(name, steps, warmup, flush=True):
         step(evs[i])
     torch.cuda.synchronize()
     dec = _stats([e[0].elapsed_time(e[1]) for e in evs])[0]
-    core = _stats([e[0].elapsed_time(e[2]) for e in evs])[0]
+    core, p10, p90 = _stats([e[0].elapsed_time(e[2]) for e in evs])
     bpt = mla.gqla_cache_scalars_per_token(sh) * 2
     return {"workload": name, "path": "gqa", "decode_ms": dec, "core_ms": core,
+            "core_ms_p10_p90": [p10, p90],
             "tokens_per_s": inp.total_tokens / (core * 1e-3),
+            "tokens": inp.total_tokens, "bytes_per_token": bpt,
             "decode_GBs": inp.total_tokens * bpt / (dec * 1e-3) / 1e9,
             "kernel": "mfma" if mla.gqla_decode_kernel_kind(sh) == 1 else "generic"}
 
@@ -224,6 +241,23 @@ def main():
         copy_calibration()
         return
     import head_latent_attention_02_amd as mla
+
+    if args.path == "gqa":
+        g = time_gqa_path(args.workload, args.steps, args.warmup, flush=not args.no_flush)
+        ach = g["decode_GBs"]
+        print(json.dumps({
+            "metric": "GQLA GQA-path decode cached tokens/s (expanded per-group cache), 1 GPU",
+            "value": g["tokens_per_s"], "unit": "cached-tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": g["core_ms"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) latents expanded on the GPU, permuted page table)",
+            "config": {"workload": args.workload, "path": "gqa", "kernel": g["kernel"],
+                       "llc_flush_between_steps": not args.no_flush},
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "gqla_decode_gqa", "kernel_ms": g["decode_ms"]}}),
+              flush=True)
+        return
 
     inp, d, ms, wall_ms = time_workload(args.workload, args.steps, args.warmup, args.splits,
                                         flush=not args.no_flush)

@@ -8,34 +8,34 @@
 // query the keys are never decompressed; AI Radio episode on GQLA, "Key concepts": on
 // the MQA-absorb path the latent is the shared key and value).
 //
-// Work decomposition (one workgroup = one sequence b, one chunk u, ROWS = 32*NQ query
-// rows, rows being the flattened (s, h) pairs):
-//  * NQ "score" waves each own 32 query rows.  Their q_abs rows stay in registers as the
-//    B operand of v_mfma_f32_32x32x16_bf16.  Per 32-token tile they load the 32 cache
-//    rows (576 bf16 each) from HBM straight into A-operand registers, 16 bytes per lane
-//    and K-step, and compute S^T[token][row] over the 576-wide contraction.  The loads of
-//    tile k+1 are issued into each register right after its MFMA has consumed it, so a
-//    whole tile of loads is always in flight.  Each score wave also writes its share of
-//    the tile's 512 latent columns to LDS for the value product.
-//  * The same score waves run the online softmax in the log2 domain with a lazy
-//    reference: the per-row reference maximum only moves when a score exceeds it by more
-//    than a slack of 32 (P then stays below 2^32, far inside bf16/fp32 range; numerator
-//    and denominator share the reference, so the result is exact).  They publish P (bf16)
-//    and a per-row factor (1 unless the reference moved) through LDS.
-//  * NQ "value" waves each own 512/NQ latent columns of O^T for all ROWS rows
-//    (accumulators in AGPRs).  They read the latent tile transposed with
-//    ds_read_b64_tr_b16 as the A operand and P^T as the B operand.  When a reference
-//    moved (rare), they fold their accumulators, rescaled, into the workgroup's own
-//    o_part slot and restart from zero; the epilogue adds the folded part back.
-//  * Score waves work on tile k while value waves work on tile k-1 (double-buffered LDS),
-//    with one workgroup barrier per tile.
-// LDS traffic per 32-token tile is ~76 KB against ~1.3k cycles of MFMA work per SIMD,
-// so neither LDS (~128 B/clk/CU) nor the vector memory path limits the loop.
+// Two kernels, both one workgroup per (sequence b, chunk u, block of query rows), rows
+// being the flattened (s, h) pairs, and both using v_mfma_f32_32x32x16_bf16 for the two
+// contractions: S^T[token][row] = C_tile . q_abs^T over the 576-wide row, and
+// O^T[latent][row] += C_tile^T . P^T over the tile's 32 tokens.
+//
+// Ring kernel (rows a multiple of 64; 256 threads, one workgroup per CU):
+//  * The chunk streams through a 4-deep LDS ring of 32-token tiles (36 KB each), filled
+//    two tiles ahead by global_load_lds_dwordx4 (HBM -> LDS, no register staging).  All
+//    four waves issue a quarter of every tile's loads; rows land XOR-swizzled by 16-byte
+//    chunk so both the row-wise and the transposed reads are free of bank conflicts.
+//  * Waves 0 and 1 are score waves (32 rows each, q_abs held in registers as the B
+//    operand); they compute tile k's scores, run the softmax and publish P (bf16).
+//  * Waves 2 and 3 are value waves (256 latent columns each, O^T in 256 AGPRs); they
+//    consume tile k-1, reading it transposed with ds_read_b64_tr_b16.
+//  * One workgroup barrier per tile.  The softmax keeps a lazy per-row reference: it
+//    only moves when a score exceeds it by more than a slack of 32 (log2 units), so P
+//    stays below 2^32 and the accumulators never need rescaling; when a reference must
+//    move, the whole chunk is rerun from its first tile with the raised reference (rare:
+//    each rerun strictly raises a reference, at most n_tiles reruns).
+//  * The two 64-row blocks of one (b, u) are 8 workgroups apart in the grid so that they
+//    run on the same XCD and the second one's tile reads hit its L2.
+// Rows32 kernel (rows a multiple of 32, e.g. 32 GQLA heads at s_q = 1): one score wave
+// loads cache rows straight into A-operand registers and stages the latent columns for
+// one value wave through a double-buffered LDS tile, same softmax scheme.
 //
 // Rows past a sequence's end in its last page are never used: their loads are clamped to
 // the tile's first row (a valid token) and their scores masked, so NaN padding cannot
-// reach the output.  Grid: the two row blocks of one (b, u) are 8 workgroups apart so
-// that they land on the same XCD and share its L2.
+// reach the output.
 #include <math.h>
 #include <stdlib.h>
 
