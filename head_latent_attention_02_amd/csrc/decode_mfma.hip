@@ -400,7 +400,7 @@ constexpr int kRowB = kD * 2;              // 1152 bytes per cache row
 constexpr int kTileB = kTT * kRowB;        // 36864 bytes per tile
 constexpr int kNB = 4;                     // ring depth in tiles
 constexpr int kAhead = 2;                  // tiles loaded ahead of the score waves
-constexpr int kDmaPerWave = kTileB / 1024 / 4;   // 9 of 36 1-KB loads per tile per wave
+constexpr int kLoadsPerWave = kTileB / 1024 / 4;   // 9 of 36 1-KB loads per tile per wave
 
 struct Smem {
   char ring[kNB][kTileB];
@@ -409,36 +409,37 @@ struct Smem {
   int restart;
 };
 
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_block) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_block) : "memory", "m0");
-}
+// One wave's share of a tile, in registers between its global loads and its LDS stores.
+struct Stage {
+  u32x4 r[kLoadsPerWave];
+};
 
 // Ring byte 16*c of a tile holds chunk (c % 72) ^ swz(c / 72) of tile row c / 72; load j
-// of wave `wave` moves ring bytes [1024 (wave + 4 j), +1024), 16 per lane.
-// Wave `wave`'s share of tile kt into ring slot kt % kNB.  Rows past the chunk end (only
+// of wave `wave` covers ring bytes [1024 (wave + 4 j), +1024), 16 per lane, so each load
+// instruction reads about 1 KB of consecutive cache rows.  Rows past the chunk end (only
 // in a chunk's last tile) read the tile's first row instead: valid data, masked later.
-__device__ __forceinline__ void load_tile(Smem& sm, const Work& w, int lane, int kt, int wave) {
+__device__ __forceinline__ void load_stage(Stage& st, const Work& w, int lane, int kt,
+                                           int wave) {
   const int t0 = __builtin_amdgcn_readfirstlane(w.lo + kt * kTT);
   const int page = w.ptb[t0 >> 6];
   const bf16_t* base = w.pool + (static_cast<size_t>(page) * kPage + (t0 & (kPage - 1))) * kD;
   const int valid = w.hi - t0;
-  const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) char*)(&sm.ring[kt & (kNB - 1)][0])));
-  // the per-load offsets are recomputed from an opaque lane id on every call: a handful
-  // of ALU ops, instead of nine registers held across the whole chunk loop
-  int ln = lane;
-  asm volatile("" : "+v"(ln));
 #pragma unroll
-  for (int j = 0; j < kDmaPerWave; ++j) {
-    const int c = (wave + 4 * j) * 64 + ln;
+  for (int j = 0; j < kLoadsPerWave; ++j) {
+    const int c = (wave + 4 * j) * 64 + lane;
     const int row = c / 72;
-    // rows past the chunk end (only in its last tile) read the tile's first row instead:
-    // valid data, masked later
-    const int o = (row < valid) ? row * kD + ((c - row * 72) ^ swz(row)) * 8
-                                : ((c - row * 72) ^ swz(row)) * 8;
-    dma16(base + o, __builtin_amdgcn_readfirstlane(dst + (wave + 4 * j) * 1024));
+    const int ch = (c - row * 72) ^ swz(row);
+    const int o = ((row < valid) ? row * kD : 0) + ch * 8;
+    st.r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + o));
   }
+}
+
+__device__ __forceinline__ void store_stage(Smem& sm, const Stage& st, int lane, int kt,
+                                            int wave) {
+  char* dst = &sm.ring[kt & (kNB - 1)][0];
+#pragma unroll
+  for (int j = 0; j < kLoadsPerWave; ++j)
+    *reinterpret_cast<u32x4*>(dst + (wave + 4 * j) * 1024 + lane * 16) = st.r[j];
 }
 
 __device__ __forceinline__ float xhalf_max(float v) {
@@ -499,25 +500,26 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
   const bf16_t* qp = w.q_abs + (w.qrow0 + 32 * QW + n32) * kD + 8 * g;
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
-  // q_abs has landed before any ring load is issued, so the compiler's view of the
-  // vector-memory counter stays exact (it does not see the asm ring loads)
-  wait_vmcnt<0>();
   const int sw = swz(n32);
   int rb[4];                         // byte offset of chunk 2b+g of this lane's row
 #pragma unroll
   for (int b4 = 0; b4 < 4; ++b4) rb[b4] = n32 * kRowB + 16 * ((2 * b4 + g) ^ sw);
   float m_ref = -INFINITY, l_run = 0.f;
   int reruns = 0;   // each rerun passes its triggering tile, so at most n_tiles happen
+  Stage stg;
   while (true) {
     l_run = 0.f;
-    if (w.n_tiles > 0) load_tile(sm, w, lane, 0, QW);
-    if (w.n_tiles > 1) load_tile(sm, w, lane, 1, QW);
-    if (w.n_tiles > 1) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
+    for (int kt = 0; kt < min(kAhead, w.n_tiles); ++kt) {
+      load_stage(stg, w, lane, kt, QW);
+      store_stage(sm, stg, lane, kt, QW);
+    }
     __syncthreads();
     bool restarted = false;
     for (int k = 0; k <= w.n_tiles; ++k) {
+      // tile k+2's loads are in flight in registers for the whole slot
       const bool more = k + kAhead < w.n_tiles;
-      if (more) load_tile(sm, w, lane, k + kAhead, QW);
+      if (more) load_stage(stg, w, lane, k + kAhead, QW);
+      __builtin_amdgcn_sched_barrier(0);
       if (k < w.n_tiles) {
         const char* tb = &sm.ring[k & (kNB - 1)][0];
         f32x16 sacc = {};
@@ -549,8 +551,8 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
           softmax_tile<false>(sacc, lim, w.zscale, w.slack, m_ref, l_run, move, prow, g);
         if (__builtin_amdgcn_ballot_w64(move) && reruns <= w.n_tiles) sm.restart = 1;
       }
-      // this wave's loads of tile k+1 have landed (only tile k+2's may be in flight)
-      if (more) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) store_stage(sm, stg, lane, k + kAhead, QW);
       __syncthreads();
       if (check_restart(sm)) {
         restarted = true;
@@ -559,7 +561,6 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
     }
     if (!restarted) break;
     ++reruns;
-    wait_vmcnt<0>();
   }
   const float l_tot = xhalf_sum(l_run);
   if (g == 0) {
@@ -653,20 +654,21 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
         trofs[par][kt][h4] = tok * kRowB + (((col >> 3) ^ swz(tok)) * 16) + (col & 7) * 2;
       }
   const int n = w.n_tiles;
+  Stage stg;
   while (true) {
-    if (n > 0) load_tile(sm, w, lane, 0, wave);
-    if (n > 1) load_tile(sm, w, lane, 1, wave);
-    if (n > 1) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
+    for (int kt = 0; kt < min(kAhead, n); ++kt) {
+      load_stage(stg, w, lane, kt, wave);
+      store_stage(sm, stg, lane, kt, wave);
+    }
     __syncthreads();
     // slot 0: the score waves work on tile 0
     bool more = kAhead < n;
-    if (more) load_tile(sm, w, lane, kAhead, wave);
-    if (more) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
-    __syncthreads();
-    if (check_restart(sm)) {
-      wait_vmcnt<0>();
-      continue;
+    if (more) {
+      load_stage(stg, w, lane, kAhead, wave);
+      store_stage(sm, stg, lane, kAhead, wave);
     }
+    __syncthreads();
+    if (check_restart(sm)) continue;
     if (n == 0) {
       __syncthreads();   // the score waves have published the row sums
       float* orow0 = w.o_part + (w.qrow0 * w.S + w.u) * kDC + lat0 + 4 * g;
@@ -679,21 +681,24 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
     // slot 1 (peeled, so the accumulators are first written outside the loop)
     f32x16 acc[8][2];
     more = 1 + kAhead < n;
-    if (more) load_tile(sm, w, lane, 1 + kAhead, wave);
+    if (more) load_stage(stg, w, lane, 1 + kAhead, wave);
+    __builtin_amdgcn_sched_barrier(0);
     value_ring_tile<true>(sm, 0, 0, trofs, n32, g, acc);
-    if (more) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) store_stage(sm, stg, lane, 1 + kAhead, wave);
     __syncthreads();
     bool restarted = check_restart(sm);
     for (int k = 2; k <= n && !restarted; ++k) {
       more = k + kAhead < n;
-      if (more) load_tile(sm, w, lane, k + kAhead, wave);
+      if (more) load_stage(stg, w, lane, k + kAhead, wave);
+      __builtin_amdgcn_sched_barrier(0);
       value_ring_tile<false>(sm, (k - 1) & (kNB - 1), (k - 1) & 1, trofs, n32, g, acc);
-      if (more) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) store_stage(sm, stg, lane, k + kAhead, wave);
       __syncthreads();
       restarted = check_restart(sm);
     }
     if (restarted) {
-      wait_vmcnt<0>();
       continue;
     }
     __syncthreads();   // the score waves have published the row sums
