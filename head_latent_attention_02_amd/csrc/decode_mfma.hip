@@ -402,44 +402,95 @@ constexpr int kNB = 4;                     // ring depth in tiles
 constexpr int kAhead = 2;                  // tiles loaded ahead of the score waves
 constexpr int kLoadsPerWave = kTileB / 1024 / 4;   // 9 of 36 1-KB loads per tile per wave
 
+// XOR swizzle of the 16-byte chunk index inside a ring row (rows are 1152 bytes, so
+// consecutive rows start half a bank cycle apart).  Score reads take one chunk from each
+// of 16 consecutive rows: rows of equal parity get 8 distinct chunks, so a 16-lane pass
+// is conflict-free.  Transposed reads take two chunks from each of 4 consecutive rows
+// aligned to 4: rows t and t+2 differ in swizzle bits 1-2, so they never share a pair.
+// (Measured on gfx950: 130 B/clk/CU for the score pattern vs 98 with a swizzle that only
+// separates 8 consecutive rows.)
+__device__ __forceinline__ int rswz(int tok) { return (((tok >> 1) & 1) << 2) | ((tok >> 2) & 3); }
+
 struct Smem {
   char ring[kNB][kTileB];
   bf16_t pbuf[2][64 * kPRow];
   float lfin[64];
-  int restart;
+  long long flag[2];   // rerun requests: tag of (pass, tile) of the tile that asked
 };
+
+// A score wave that must move a reference at tile k writes tag(pass, k) into flag[k & 1]
+// during slot k.  Every wave reads that word right after the barrier ending slot k and
+// acts on it at the barrier ending slot k+1: the word is stable during slot k+1 (the next
+// write to it is in slot k+2), so all waves agree without extra barriers, and tags of an
+// abandoned pass never match the next one.  The request is honoured one slot late, which
+// only wastes that slot's work.
+__device__ __forceinline__ long long rerun_tag(int pass, int k) {
+  return (static_cast<long long>(pass) << 32) | static_cast<unsigned>(k);
+}
 
 // One wave's share of a tile, in registers between its global loads and its LDS stores.
+// Which waves stream the tiles: all four (a quarter each), or only the two value waves
+// (half each).  The value waves do it: the score waves' slot (36 MFMAs + the softmax) is
+// the longer one, and their load issue and LDS stores measured ~1.1k cycles per slot.
+#ifndef RING_SCORE_LOADS
+#define RING_SCORE_LOADS 0
+#endif
+constexpr bool kScoreLoads = RING_SCORE_LOADS != 0;
+constexpr int kValueLoads = kScoreLoads ? kLoadsPerWave : 2 * kLoadsPerWave;
+
+template <int NL>
 struct Stage {
-  u32x4 r[kLoadsPerWave];
+  u32x4 r[NL];
 };
 
-// Ring byte 16*c of a tile holds chunk (c % 72) ^ swz(c / 72) of tile row c / 72; load j
-// of wave `wave` covers ring bytes [1024 (wave + 4 j), +1024), 16 per lane, so each load
-// instruction reads about 1 KB of consecutive cache rows.  Rows past the chunk end (only
-// in a chunk's last tile) read the tile's first row instead: valid data, masked later.
-__device__ __forceinline__ void load_stage(Stage& st, const Work& w, int lane, int kt,
-                                           int wave) {
+// Ring byte 16*c of a tile holds chunk (c % 72) ^ rswz(c / 72) of tile row c / 72; load j
+// of a wave covers ring bytes [1024 (first + stride j), +1024), 16 per lane, so each load
+// instruction reads about 1 KB of consecutive cache rows.  The loads go through a buffer
+// resource whose base is the tile's first row and whose size is the tile's valid rows:
+// the per-lane byte offsets are fixed for the whole kernel (one register per load), and
+// rows past a chunk's end (only in its last tile) read as zeros, which are masked later.
+template <int NL>
+struct LoadPlan {
+  uint32_t off[NL];
+};
+
+template <int NL>
+__device__ __forceinline__ LoadPlan<NL> make_plan(int lane, int first, int stride) {
+  LoadPlan<NL> p;
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int c = (first + stride * j) * 64 + lane;
+    const int row = c / 72;
+    p.off[j] = static_cast<uint32_t>(row * kD + (((c - row * 72) ^ rswz(row)) * 8)) * 2u;
+  }
+  return p;
+}
+
+// gfx9 buffer resource word 3 for raw (untyped) dword access
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kSlc = 2;   // streaming (non-temporal) cache policy
+
+template <int NL>
+__device__ __forceinline__ void load_stage(Stage<NL>& st, const LoadPlan<NL>& plan,
+                                           const Work& w, int kt) {
   const int t0 = __builtin_amdgcn_readfirstlane(w.lo + kt * kTT);
   const int page = w.ptb[t0 >> 6];
   const bf16_t* base = w.pool + (static_cast<size_t>(page) * kPage + (t0 & (kPage - 1))) * kD;
-  const int valid = w.hi - t0;
+  const int valid = min(w.hi - t0, kTT);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(base), 0, valid * kRowB, kBufWord3);
 #pragma unroll
-  for (int j = 0; j < kLoadsPerWave; ++j) {
-    const int c = (wave + 4 * j) * 64 + lane;
-    const int row = c / 72;
-    const int ch = (c - row * 72) ^ swz(row);
-    const int o = ((row < valid) ? row * kD : 0) + ch * 8;
-    st.r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + o));
-  }
+  for (int j = 0; j < NL; ++j)
+    st.r[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, plan.off[j], 0, kSlc);
 }
 
-__device__ __forceinline__ void store_stage(Smem& sm, const Stage& st, int lane, int kt,
-                                            int wave) {
+template <int NL>
+__device__ __forceinline__ void store_stage(Smem& sm, const Stage<NL>& st, int lane, int kt,
+                                            int first, int stride) {
   char* dst = &sm.ring[kt & (kNB - 1)][0];
 #pragma unroll
-  for (int j = 0; j < kLoadsPerWave; ++j)
-    *reinterpret_cast<u32x4*>(dst + (wave + 4 * j) * 1024 + lane * 16) = st.r[j];
+  for (int j = 0; j < NL; ++j)
+    *reinterpret_cast<u32x4*>(dst + (first + stride * j) * 1024 + lane * 16) = st.r[j];
 }
 
 __device__ __forceinline__ float xhalf_max(float v) {
@@ -500,31 +551,38 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
   const bf16_t* qp = w.q_abs + (w.qrow0 + 32 * QW + n32) * kD + 8 * g;
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
-  const int sw = swz(n32);
+  const int sw = rswz(n32);
   int rb[4];                         // byte offset of chunk 2b+g of this lane's row
 #pragma unroll
   for (int b4 = 0; b4 < 4; ++b4) rb[b4] = n32 * kRowB + 16 * ((2 * b4 + g) ^ sw);
   float m_ref = -INFINITY, l_run = 0.f;
   int reruns = 0;   // each rerun passes its triggering tile, so at most n_tiles happen
-  Stage stg;
+  Stage<kLoadsPerWave> stg;
+  const LoadPlan<kLoadsPerWave> plan = make_plan<kLoadsPerWave>(lane, QW, 4);
   while (true) {
     l_run = 0.f;
-    for (int kt = 0; kt < min(kAhead, w.n_tiles); ++kt) {
-      load_stage(stg, w, lane, kt, QW);
-      store_stage(sm, stg, lane, kt, QW);
+    if (kScoreLoads) {
+      for (int kt = 0; kt < min(kAhead, w.n_tiles); ++kt) {
+        load_stage(stg, plan, w, kt);
+        store_stage(sm, stg, lane, kt, QW, 4);
+      }
     }
     __syncthreads();
     bool restarted = false;
     for (int k = 0; k <= w.n_tiles; ++k) {
+      const long long seen = (k > 0) ? sm.flag[(k - 1) & 1] : -1;
       // tile k+2's loads are in flight in registers for the whole slot
-      const bool more = k + kAhead < w.n_tiles;
-      if (more) load_stage(stg, w, lane, k + kAhead, QW);
+      const bool more = kScoreLoads && k + kAhead < w.n_tiles;
+      if (more) load_stage(stg, plan, w, k + kAhead);
       __builtin_amdgcn_sched_barrier(0);
       if (k < w.n_tiles) {
         const char* tb = &sm.ring[k & (kNB - 1)][0];
         f32x16 sacc = {};
         // A operands run kPF K-steps ahead of the MFMA that consumes them
-        constexpr int kPF = 8;
+#ifndef SCORE_PF
+#define SCORE_PF 8
+#endif
+        constexpr int kPF = SCORE_PF;
         bf16x8 abuf[kPF];
 #pragma unroll
         for (int ks = 0; ks < kPF; ++ks)
@@ -549,12 +607,14 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
           softmax_tile<true>(sacc, lim, w.zscale, w.slack, m_ref, l_run, move, prow, g);
         else
           softmax_tile<false>(sacc, lim, w.zscale, w.slack, m_ref, l_run, move, prow, g);
-        if (__builtin_amdgcn_ballot_w64(move) && reruns <= w.n_tiles) sm.restart = 1;
+        if (__builtin_amdgcn_ballot_w64(move) && reruns <= w.n_tiles)
+          sm.flag[k & 1] = rerun_tag(reruns, k);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (more) store_stage(sm, stg, lane, k + kAhead, QW);
+      if (more) store_stage(sm, stg, lane, k + kAhead, QW, 4);
+      const bool rerun = k > 0 && seen == rerun_tag(reruns, k - 1);
       __syncthreads();
-      if (check_restart(sm)) {
+      if (rerun) {
         restarted = true;
         break;
       }
@@ -651,24 +711,28 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
       for (int h4 = 0; h4 < 2; ++h4) {
         const int col = lat0 + 32 * par + m_base + 4 * (L & 3);
         const int tok = 16 * kt + 8 * g16 + 4 * h4 + (L >> 2);
-        trofs[par][kt][h4] = tok * kRowB + (((col >> 3) ^ swz(tok)) * 16) + (col & 7) * 2;
+        trofs[par][kt][h4] = tok * kRowB + (((col >> 3) ^ rswz(tok)) * 16) + (col & 7) * 2;
       }
   const int n = w.n_tiles;
-  Stage stg;
+  // this wave's loads: blocks first, first + stride, ... of every tile
+  constexpr int first = kScoreLoads ? wave : VW;
+  constexpr int stride = kScoreLoads ? 4 : 2;
+  Stage<kValueLoads> stg;
+  const LoadPlan<kValueLoads> plan = make_plan<kValueLoads>(lane, first, stride);
+  int reruns = 0;
   while (true) {
     for (int kt = 0; kt < min(kAhead, n); ++kt) {
-      load_stage(stg, w, lane, kt, wave);
-      store_stage(sm, stg, lane, kt, wave);
+      load_stage(stg, plan, w, kt);
+      store_stage(sm, stg, lane, kt, first, stride);
     }
     __syncthreads();
     // slot 0: the score waves work on tile 0
     bool more = kAhead < n;
     if (more) {
-      load_stage(stg, w, lane, kAhead, wave);
-      store_stage(sm, stg, lane, kAhead, wave);
+      load_stage(stg, plan, w, kAhead);
+      store_stage(sm, stg, lane, kAhead, first, stride);
     }
     __syncthreads();
-    if (check_restart(sm)) continue;
     if (n == 0) {
       __syncthreads();   // the score waves have published the row sums
       float* orow0 = w.o_part + (w.qrow0 * w.S + w.u) * kDC + lat0 + 4 * g;
@@ -680,25 +744,28 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
     }
     // slot 1 (peeled, so the accumulators are first written outside the loop)
     f32x16 acc[8][2];
+    long long seen = sm.flag[0];
     more = 1 + kAhead < n;
-    if (more) load_stage(stg, w, lane, 1 + kAhead, wave);
+    if (more) load_stage(stg, plan, w, 1 + kAhead);
     __builtin_amdgcn_sched_barrier(0);
     value_ring_tile<true>(sm, 0, 0, trofs, n32, g, acc);
     __builtin_amdgcn_sched_barrier(0);
-    if (more) store_stage(sm, stg, lane, 1 + kAhead, wave);
+    if (more) store_stage(sm, stg, lane, 1 + kAhead, first, stride);
+    bool restarted = seen == rerun_tag(reruns, 0);
     __syncthreads();
-    bool restarted = check_restart(sm);
     for (int k = 2; k <= n && !restarted; ++k) {
+      seen = sm.flag[(k - 1) & 1];
       more = k + kAhead < n;
-      if (more) load_stage(stg, w, lane, k + kAhead, wave);
+      if (more) load_stage(stg, plan, w, k + kAhead);
       __builtin_amdgcn_sched_barrier(0);
       value_ring_tile<false>(sm, (k - 1) & (kNB - 1), (k - 1) & 1, trofs, n32, g, acc);
       __builtin_amdgcn_sched_barrier(0);
-      if (more) store_stage(sm, stg, lane, k + kAhead, wave);
+      if (more) store_stage(sm, stg, lane, k + kAhead, first, stride);
+      restarted = seen == rerun_tag(reruns, k - 1);
       __syncthreads();
-      restarted = check_restart(sm);
     }
     if (restarted) {
+      ++reruns;
       continue;
     }
     __syncthreads();   // the score waves have published the row sums
@@ -760,7 +827,7 @@ void decode_absorbed_mfma_ring_kernel(
   w.zscale = zscale;
   w.slack = slack;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (threadIdx.x == 0) sm.restart = 0;
+  if (threadIdx.x == 0) sm.flag[0] = sm.flag[1] = -1;
   __syncthreads();
   if (wave == 0)
     ring::score_wave<0>(sm, w, lane);
