@@ -39,6 +39,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -399,8 +401,7 @@ namespace ring {
 constexpr int kRowB = kD * 2;              // 1152 bytes per cache row
 constexpr int kTileB = kTT * kRowB;        // 36864 bytes per tile
 constexpr int kNB = 4;                     // ring depth in tiles
-constexpr int kAhead = 2;                  // tiles loaded ahead of the score waves
-constexpr int kLoadsPerWave = kTileB / 1024 / 4;   // 9 of 36 1-KB loads per tile per wave
+constexpr int kLoads = kTileB / 1024 / 2;  // 18 of a tile's 36 1-KB loads per value wave
 
 // XOR swizzle of the 16-byte chunk index inside a ring row (rows are 1152 bytes, so
 // consecutive rows start half a bank cycle apart).  Score reads take one chunk from each
@@ -416,6 +417,7 @@ struct Smem {
   bf16_t pbuf[2][64 * kPRow];
   float lfin[64];
   long long flag[2];   // rerun requests: tag of (pass, tile) of the tile that asked
+  uint32_t plan[2][kLoads / 2][64];   // value wave VW's per-lane load offsets
 };
 
 // A score wave that must move a reference at tile k writes tag(pass, k) into flag[k & 1]
@@ -429,15 +431,6 @@ __device__ __forceinline__ long long rerun_tag(int pass, int k) {
 }
 
 // One wave's share of a tile, in registers between its global loads and its LDS stores.
-// Which waves stream the tiles: all four (a quarter each), or only the two value waves
-// (half each).  The value waves do it: the score waves' slot (36 MFMAs + the softmax) is
-// the longer one, and their load issue and LDS stores measured ~1.1k cycles per slot.
-#ifndef RING_SCORE_LOADS
-#define RING_SCORE_LOADS 0
-#endif
-constexpr bool kScoreLoads = RING_SCORE_LOADS != 0;
-constexpr int kValueLoads = kScoreLoads ? kLoadsPerWave : 2 * kLoadsPerWave;
-
 template <int NL>
 struct Stage {
   u32x4 r[NL];
@@ -449,39 +442,47 @@ struct Stage {
 // resource whose base is the tile's first row and whose size is the tile's valid rows:
 // the per-lane byte offsets are fixed for the whole kernel (one register per load), and
 // rows past a chunk's end (only in its last tile) read as zeros, which are masked later.
-template <int NL>
-struct LoadPlan {
-  uint32_t off[NL];
-};
+// Block b + 18 holds the same chunks as block b, 16 rows (18432 bytes) further down (the
+// swizzle ignores row bit 4), so a wave's 18 loads need only 9 offset registers.  The
+// distance is added to the per-lane offset (not passed as the scalar offset), so the
+// buffer's range check, which covers the per-lane offset, still zeroes rows past the end.
+constexpr int kHalfRowsB = 16 * kRowB;
 
-template <int NL>
-__device__ __forceinline__ LoadPlan<NL> make_plan(int lane, int first, int stride) {
-  LoadPlan<NL> p;
+// The offsets sit in LDS (read back once per tile), which keeps 9 registers free in the
+// value waves: their loop is one register short of spilling otherwise.
+__device__ __forceinline__ void make_plan(uint32_t (&pl)[kLoads / 2][64], int lane, int vw) {
 #pragma unroll
-  for (int j = 0; j < NL; ++j) {
-    const int c = (first + stride * j) * 64 + lane;
+  for (int j = 0; j < kLoads / 2; ++j) {
+    const int c = (vw + 2 * j) * 64 + lane;
     const int row = c / 72;
-    p.off[j] = static_cast<uint32_t>(row * kD + (((c - row * 72) ^ rswz(row)) * 8)) * 2u;
+    pl[j][lane] = static_cast<uint32_t>(row * kD + (((c - row * 72) ^ rswz(row)) * 8)) * 2u;
   }
-  return p;
 }
 
 // gfx9 buffer resource word 3 for raw (untyped) dword access
 constexpr int kBufWord3 = 0x00020000;
 constexpr int kSlc = 2;   // streaming (non-temporal) cache policy
 
-template <int NL>
-__device__ __forceinline__ void load_stage(Stage<NL>& st, const LoadPlan<NL>& plan,
-                                           const Work& w, int kt) {
+// Value wave vw's loads: j < 9 cover blocks vw + 2 j, j >= 9 the blocks 18 further on.
+__device__ __forceinline__ void load_stage(Stage<kLoads>& st,
+                                           const uint32_t (&pl)[kLoads / 2][64],
+                                           const Work& w, int kt, int lane) {
   const int t0 = __builtin_amdgcn_readfirstlane(w.lo + kt * kTT);
-  const int page = w.ptb[t0 >> 6];
+  // wave-uniform (readfirstlane): the buffer resource must live in scalar registers
+  const int valid = __builtin_amdgcn_readfirstlane(max(min(w.hi - t0, kTT), 0));
+  // an empty chunk (valid == 0) reads nothing, not even its page-table entry
+  int page = 0;
+  if (valid > 0) page = w.ptb[t0 >> 6];
   const bf16_t* base = w.pool + (static_cast<size_t>(page) * kPage + (t0 & (kPage - 1))) * kD;
-  const int valid = min(w.hi - t0, kTT);
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16_t*>(base), 0, valid * kRowB, kBufWord3);
 #pragma unroll
-  for (int j = 0; j < NL; ++j)
-    st.r[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, plan.off[j], 0, kSlc);
+  for (int j = 0; j < kLoads / 2; ++j) {
+    const uint32_t off = pl[j][lane];
+    st.r[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kSlc);
+    st.r[j + kLoads / 2] =
+        __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + kHalfRowsB, 0, kSlc);
+  }
 }
 
 template <int NL>
@@ -541,7 +542,92 @@ __device__ __forceinline__ void softmax_tile(const f32x16& sacc, int lim, float 
   }
 }
 
-// Score wave QW (rows 32 QW .. 32 QW + 31).  Slot k: scores and P of tile k.
+// One score-wave slot: the 36 MFMAs of S^T for the tile at `tb` (into sacc_out) and the
+// softmax of the previous tile's scores (sacc_in).  The softmax is cut into pieces of a
+// few VALU instructions that sit between consecutive MFMAs, where they issue while the
+// matrix core is busy (gfx950 hides about four VALU instructions behind each 32x32x16
+// MFMA; larger pieces stall it).  Lane (row n32, half g) holds tokens 8 (j / 4) + 4 g +
+// j % 4 of a tile; lim = visible tokens of its row there (MASK: some lane has lim < 32).
+template <bool DO_MFMA, bool DO_SOFT, bool MASK>
+__device__ __forceinline__ void score_slot(const char* tb, const bf16x8 (&qreg)[kKS],
+                                           const int (&rb)[4], f32x16& sacc_out,
+                                           const f32x16& sacc_in, int lim, float zscale,
+                                           float slack, float& m_ref, float& l_run,
+                                           bool& move, bf16_t* prow, int g) {
+  // A operands run kPF K-steps ahead of the MFMA that consumes them
+  constexpr int kPF = 8;
+  bf16x8 abuf[kPF];
+  f32x16 acc = {};
+  if (DO_MFMA) {
+#pragma unroll
+    for (int ks = 0; ks < kPF; ++ks)
+      abuf[ks] = *reinterpret_cast<const bf16x8*>(tb + rb[ks & 3] + 128 * (ks >> 2));
+  }
+  float z[16], mx4[4];
+  float nm = 0.f;
+  bool live = false;
+  uint32_t pk[2];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    if (DO_MFMA) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abuf[ks % kPF], qreg[ks], acc, 0, 0, 0);
+      if (ks + kPF < kKS) {
+        const int kn = ks + kPF;
+        abuf[ks % kPF] = *reinterpret_cast<const bf16x8*>(tb + rb[kn & 3] + 128 * (kn >> 2));
+      }
+    }
+    if (DO_SOFT) {
+      if (ks < 4) {                       // scores out of the accumulators (masked)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 4 * ks + i;
+          z[j] = sacc_in[j];
+          if (MASK && !(8 * ks + 4 * g + i < lim)) z[j] = -INFINITY;
+        }
+      } else if (ks < 8) {                // row maximum, four at a time
+        const int q = ks - 4;
+        mx4[q] = fmaxf(fmaxf(z[4 * q], z[4 * q + 1]), fmaxf(z[4 * q + 2], z[4 * q + 3]));
+      } else if (ks == 8) {
+        const float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+        mx4[0] = xhalf_max(mx * zscale);
+      } else if (ks == 9) {
+        // The first visible tile of a row fixes its reference; a later jump past the
+        // slack raises it to this tile's maximum and asks for a rerun, so a rerun can
+        // never trigger twice on the same tile: every rerun raises some reference.
+        const float mt = mx4[0];
+        move = m_ref != -INFINITY && mt > m_ref + slack;
+        if (m_ref == -INFINITY || move) m_ref = mt;
+        live = m_ref != -INFINITY;
+        nm = -m_ref;
+      } else if (ks < 18) {               // two probabilities per step, bf16 pairs
+        const int j = 2 * (ks - 10);
+        float pv[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          pv[i] = live ? __builtin_amdgcn_exp2f(fmaf(z[j + i], zscale, nm)) : 0.f;
+          l_run += pv[i];
+        }
+        pk[(j >> 1) & 1] = __builtin_bit_cast(
+            uint32_t, __builtin_shufflevector(
+                          __builtin_bit_cast(__bf16 __attribute__((ext_vector_type(1))),
+                                             static_cast<__bf16>(pv[0])),
+                          __builtin_bit_cast(__bf16 __attribute__((ext_vector_type(1))),
+                                             static_cast<__bf16>(pv[1])),
+                          0, 1));
+        if ((j & 3) == 2) {               // four tokens 8 (j / 4) + 4 g .. +3 are done
+          *reinterpret_cast<uint2*>(prow + 8 * (j >> 2) + 4 * g) = make_uint2(pk[0], pk[1]);
+        }
+      }
+    }
+    // keep the read for step ks+kPF and this step's softmax piece next to MFMA ks
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (DO_MFMA) sacc_out = acc;
+}
+
+// Score wave QW (rows 32 QW .. 32 QW + 31).  Slot s: the MFMAs of tile s and the softmax
+// (P, published to LDS) of tile s-1, so the value waves use tile s-2.
 template <int QW>
 __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
   const int n32 = lane & 31, g = lane >> 5;
@@ -555,69 +641,48 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
   int rb[4];                         // byte offset of chunk 2b+g of this lane's row
 #pragma unroll
   for (int b4 = 0; b4 < 4; ++b4) rb[b4] = n32 * kRowB + 16 * ((2 * b4 + g) ^ sw);
+  const int n = w.n_tiles;
   float m_ref = -INFINITY, l_run = 0.f;
   int reruns = 0;   // each rerun passes its triggering tile, so at most n_tiles happen
-  Stage<kLoadsPerWave> stg;
-  const LoadPlan<kLoadsPerWave> plan = make_plan<kLoadsPerWave>(lane, QW, 4);
+  f32x16 sacc[2];
+  bool restarted = false;
+  // one slot; P = parity of s (sacc[P] takes tile s, sacc[1 - P] holds tile s-1).
+  // Returns true when the pass is over (last slot done, or a rerun).
+  auto slot = [&](auto par, int s) -> bool {
+    constexpr int P = decltype(par)::value;
+    const long long seen = (s >= 2) ? sm.flag[s & 1] : -1;   // tile s-2's request
+    const bool mf = s < n, sf = s >= 1 && s <= n;
+    const char* tb = &sm.ring[s & (kNB - 1)][0];
+    const int lim = top_row - (w.lo + (s - 1) * kTT);
+    bf16_t* prow = &sm.pbuf[(s - 1) & 1][(32 * QW + n32) * kPRow];
+    bool move = false;
+    const bool masked = __builtin_amdgcn_ballot_w64(lim < kTT) != 0;
+    if (mf && sf && !masked)
+      score_slot<true, true, false>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
+                                    w.slack, m_ref, l_run, move, prow, g);
+    else if (mf && sf)
+      score_slot<true, true, true>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
+                                   w.slack, m_ref, l_run, move, prow, g);
+    else if (mf)
+      score_slot<true, false, false>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
+                                     w.slack, m_ref, l_run, move, prow, g);
+    else if (sf)
+      score_slot<false, true, true>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
+                                    w.slack, m_ref, l_run, move, prow, g);
+    if (sf && __builtin_amdgcn_ballot_w64(move) && reruns <= n)
+      sm.flag[(s - 1) & 1] = rerun_tag(reruns, s - 1);
+    const bool rerun = s >= 2 && seen == rerun_tag(reruns, s - 2);
+    __syncthreads();
+    if (rerun) restarted = true;
+    return rerun || s == n + 1;
+  };
   while (true) {
     l_run = 0.f;
-    if (kScoreLoads) {
-      for (int kt = 0; kt < min(kAhead, w.n_tiles); ++kt) {
-        load_stage(stg, plan, w, kt);
-        store_stage(sm, stg, lane, kt, QW, 4);
-      }
-    }
-    __syncthreads();
-    bool restarted = false;
-    for (int k = 0; k <= w.n_tiles; ++k) {
-      const long long seen = (k > 0) ? sm.flag[(k - 1) & 1] : -1;
-      // tile k+2's loads are in flight in registers for the whole slot
-      const bool more = kScoreLoads && k + kAhead < w.n_tiles;
-      if (more) load_stage(stg, plan, w, k + kAhead);
-      __builtin_amdgcn_sched_barrier(0);
-      if (k < w.n_tiles) {
-        const char* tb = &sm.ring[k & (kNB - 1)][0];
-        f32x16 sacc = {};
-        // A operands run kPF K-steps ahead of the MFMA that consumes them
-#ifndef SCORE_PF
-#define SCORE_PF 8
-#endif
-        constexpr int kPF = SCORE_PF;
-        bf16x8 abuf[kPF];
-#pragma unroll
-        for (int ks = 0; ks < kPF; ++ks)
-          abuf[ks] = *reinterpret_cast<const bf16x8*>(tb + rb[ks & 3] + 128 * (ks >> 2));
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks) {
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abuf[ks % kPF], qreg[ks], sacc, 0,
-                                                         0, 0);
-          if (ks + kPF < kKS) {
-            const int kn = ks + kPF;
-            abuf[ks % kPF] =
-                *reinterpret_cast<const bf16x8*>(tb + rb[kn & 3] + 128 * (kn >> 2));
-          }
-          // keep the read for step ks+kPF between MFMAs ks and ks+1
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        const int lim = top_row - (w.lo + k * kTT);
-        bf16_t* prow = &sm.pbuf[k & 1][(32 * QW + n32) * kPRow];
-        bool move;
-        if (__builtin_amdgcn_ballot_w64(lim < kTT))
-          softmax_tile<true>(sacc, lim, w.zscale, w.slack, m_ref, l_run, move, prow, g);
-        else
-          softmax_tile<false>(sacc, lim, w.zscale, w.slack, m_ref, l_run, move, prow, g);
-        if (__builtin_amdgcn_ballot_w64(move) && reruns <= w.n_tiles)
-          sm.flag[k & 1] = rerun_tag(reruns, k);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) store_stage(sm, stg, lane, k + kAhead, QW, 4);
-      const bool rerun = k > 0 && seen == rerun_tag(reruns, k - 1);
-      __syncthreads();
-      if (rerun) {
-        restarted = true;
-        break;
-      }
+    restarted = false;
+    __syncthreads();   // the value waves have stored tile 0
+    for (int s = 0;; s += 2) {
+      if (slot(std::integral_constant<int, 0>(), s)) break;
+      if (slot(std::integral_constant<int, 1>(), s + 1)) break;
     }
     if (!restarted) break;
     ++reruns;
@@ -655,7 +720,6 @@ __device__ __forceinline__ void value_ring_tile(Smem& sm, int slot, int pb_i,
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         to[a][b][c] = trofs[a][b][c];
-        asm volatile("" : "+v"(to[a][b][c]));
       }
   auto read_a = [&](int step) -> bf16x8 {
     const int mb = step >> 1, kt = step & 1;
@@ -714,24 +778,31 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
         trofs[par][kt][h4] = tok * kRowB + (((col >> 3) ^ rswz(tok)) * 16) + (col & 7) * 2;
       }
   const int n = w.n_tiles;
-  // this wave's loads: blocks first, first + stride, ... of every tile
-  constexpr int first = kScoreLoads ? wave : VW;
-  constexpr int stride = kScoreLoads ? 4 : 2;
-  Stage<kValueLoads> stg;
-  const LoadPlan<kValueLoads> plan = make_plan<kValueLoads>(lane, first, stride);
+  // this wave streams 1-KB blocks VW, VW + 2, ... of every tile.  Tile s+1 is loaded into
+  // registers during slot s-1 and stored into the ring at the start of slot s (its ring
+  // slot held tile s-3, last read by the value waves in slot s-1), so every load has a
+  // whole slot to land.  Slot s multiplies tile s-2 (its P was published in slot s-1).
+  Stage<kLoads> stg;
+  uint32_t (&plan)[kLoads / 2][64] = sm.plan[VW];
+  make_plan(plan, lane, VW);
   int reruns = 0;
   while (true) {
-    for (int kt = 0; kt < min(kAhead, n); ++kt) {
-      load_stage(stg, plan, w, kt);
-      store_stage(sm, stg, lane, kt, first, stride);
-    }
+    // Loads and stores are unconditional: past the last tile they repeat tile n-1 into
+    // ring slot (s+1) % 4, which no wave reads in slot s and no later slot needs.
+    const int last = max(n - 1, 0);
+    // prologue: tile 0 in the ring, tile 1 in registers
+    load_stage(stg, plan, w, 0, lane);
+    store_stage(sm, stg, lane, 0, VW, 2);
+    load_stage(stg, plan, w, min(1, last), lane);
     __syncthreads();
-    // slot 0: the score waves work on tile 0
-    bool more = kAhead < n;
-    if (more) {
-      load_stage(stg, plan, w, kAhead);
-      store_stage(sm, stg, lane, kAhead, first, stride);
-    }
+    // slots 0 and 1: the score waves start; tiles 1 and 2 go into the ring
+    store_stage(sm, stg, lane, 1, VW, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(stg, plan, w, min(2, last), lane);
+    __syncthreads();
+    store_stage(sm, stg, lane, 2, VW, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(stg, plan, w, min(3, last), lane);
     __syncthreads();
     if (n == 0) {
       __syncthreads();   // the score waves have published the row sums
@@ -742,26 +813,24 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
               make_float4(0.f, 0.f, 0.f, 0.f);
       return;
     }
-    // slot 1 (peeled, so the accumulators are first written outside the loop)
+    // slot 2 (peeled, so the accumulators are first written outside the loop)
     f32x16 acc[8][2];
     long long seen = sm.flag[0];
-    more = 1 + kAhead < n;
-    if (more) load_stage(stg, plan, w, 1 + kAhead);
+    store_stage(sm, stg, lane, 3, VW, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(stg, plan, w, min(4, last), lane);
     __builtin_amdgcn_sched_barrier(0);
     value_ring_tile<true>(sm, 0, 0, trofs, n32, g, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) store_stage(sm, stg, lane, 1 + kAhead, first, stride);
     bool restarted = seen == rerun_tag(reruns, 0);
     __syncthreads();
-    for (int k = 2; k <= n && !restarted; ++k) {
-      seen = sm.flag[(k - 1) & 1];
-      more = k + kAhead < n;
-      if (more) load_stage(stg, plan, w, k + kAhead);
+    for (int s = 3; s <= n + 1 && !restarted; ++s) {
+      seen = sm.flag[s & 1];
+      store_stage(sm, stg, lane, s + 1, VW, 2);
       __builtin_amdgcn_sched_barrier(0);
-      value_ring_tile<false>(sm, (k - 1) & (kNB - 1), (k - 1) & 1, trofs, n32, g, acc);
+      load_stage(stg, plan, w, min(s + 2, last), lane);
       __builtin_amdgcn_sched_barrier(0);
-      if (more) store_stage(sm, stg, lane, k + kAhead, first, stride);
-      restarted = seen == rerun_tag(reruns, k - 1);
+      value_ring_tile<false>(sm, (s - 2) & (kNB - 1), (s - 2) & 1, trofs, n32, g, acc);
+      restarted = seen == rerun_tag(reruns, s - 2);
       __syncthreads();
     }
     if (restarted) {
