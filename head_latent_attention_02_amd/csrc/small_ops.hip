@@ -18,21 +18,36 @@ namespace {
 
 constexpr int kQB = 8;  // queries per block in a1 / a4
 
-// 8 consecutive elements as floats (one 16-byte load for bf16, two for fp32)
-__device__ __forceinline__ void load8(const bf16_t* p, float (&x)[8]) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+// 8 consecutive elements: a raw chunk (one 16-byte load for bf16, two for fp32) and its
+// conversion to floats.  Kernels issue a batch of raw loads first and convert afterwards,
+// so that a whole batch is in flight at once.
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<bf16_t> {
+  uint4 v;
+};
+template <>
+struct Raw8<float> {
+  float4 a, b;
+};
+__device__ __forceinline__ Raw8<bf16_t> load_raw8(const bf16_t* p) {
+  return {*reinterpret_cast<const uint4*>(p)};
+}
+__device__ __forceinline__ Raw8<float> load_raw8(const float* p) {
+  return {*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
+}
+__device__ __forceinline__ void to_f32(const Raw8<bf16_t>& r, float (&x)[8]) {
+  const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     x[2 * i] = __uint_as_float(w[i] << 16);
     x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
   }
 }
-__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+__device__ __forceinline__ void to_f32(const Raw8<float>& r, float (&x)[8]) {
+  x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+  x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
 }
 
 // ---------------------------------------------------------------- a1 absorb
@@ -41,22 +56,29 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
 // chunk is one 512-byte coalesced read per 32 lanes, and every weight byte of the block
 // is read once.
 constexpr int kAbsCols = 256;
+constexpr int kAbsBatch = 16;   // weight rows per thread in flight at once
 template <typename T>
 __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
                                                        const T* __restrict__ w_uk,
                                                        T* __restrict__ q_abs, int NQ, int H,
                                                        int Hw, int d_n, int d_r, int d_c) {
   extern __shared__ float smem[];
-  float* qs = smem;                       // [kQB][d_n]
+  float* qs = smem;                       // [d_n][kQB]: row i's 8 queries are 32 bytes
   float* red = smem + kQB * d_n;          // [4 waves][kQB][kAbsCols]
   const int h = blockIdx.x, c0 = blockIdx.y * kAbsCols, q0 = blockIdx.z * kQB;
   const int w = h / (H / Hw);
   const int nq = min(kQB, NQ - q0);
   const int dq = d_n + d_r, D = d_c + d_r;
   const int tid = threadIdx.x, rs = tid >> 5, cl = tid & 31;
-  for (int idx = tid; idx < kQB * d_n; idx += blockDim.x) {
-    const int jq = idx / d_n, i = idx - jq * d_n;
-    qs[idx] = (jq < nq) ? ldf(q + (static_cast<size_t>(q0 + jq) * H + h) * dq + i) : 0.f;
+  // the queries' no-position parts, 8 elements per thread and load (one load each while
+  // kQB * d_n <= 8 * 256), transposed into qs
+  for (int idx = tid; idx < kQB * d_n / 8; idx += blockDim.x) {
+    const int per = d_n / 8;
+    const int jq = idx / per, i8 = 8 * (idx - jq * per);
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (jq < nq) to_f32(load_raw8(q + (static_cast<size_t>(q0 + jq) * H + h) * dq + i8), x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qs[(i8 + e) * kQB + jq] = x[e];
   }
   __syncthreads();
   const int c = c0 + 8 * cl;
@@ -67,16 +89,30 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
     for (int e = 0; e < 8; ++e) acc[jq][e] = 0.f;
   if (c < d_c) {
     const T* W = w_uk + static_cast<size_t>(w) * d_n * d_c + c;
-    // all of a thread's weight loads are issued back to back (16 in flight at d_n = 128)
-#pragma unroll 16
-    for (int i = rs; i < d_n; i += 8) {
-      float wv[8];
-      load8(W + static_cast<size_t>(i) * d_c, wv);
+    // rows rs, rs + 8, ... in batches of kAbsBatch: the batch's loads are all issued before
+    // any is used (at d_n = 128 a thread's whole share is one batch)
+    for (int i0 = rs; i0 < d_n; i0 += 8 * kAbsBatch) {
+      Raw8<T> raw[kAbsBatch];
 #pragma unroll
-      for (int jq = 0; jq < kQB; ++jq) {
-        const float qv = qs[jq * d_n + i];
+      for (int bt = 0; bt < kAbsBatch; ++bt) {
+        const int i = i0 + 8 * bt;
+        if (i < d_n) raw[bt] = load_raw8(W + static_cast<size_t>(i) * d_c);
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[jq][e] = fmaf(qv, wv[e], acc[jq][e]);
+      for (int bt = 0; bt < kAbsBatch; ++bt) {
+        const int i = i0 + 8 * bt;
+        if (i >= d_n) break;
+        float wv[8];
+        to_f32(raw[bt], wv);
+        // the row's 8 query values: two 16-byte LDS reads, the same address across a
+        // half-wave (a broadcast)
+        const float4 qa = *reinterpret_cast<const float4*>(&qs[i * kQB]);
+        const float4 qb = *reinterpret_cast<const float4*>(&qs[i * kQB + 4]);
+        const float qv[kQB] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+        for (int jq = 0; jq < kQB; ++jq)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[jq][e] = fmaf(qv[jq], wv[e], acc[jq][e]);
       }
     }
   }
@@ -112,6 +148,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
 }
 
 // ---------------------------------------------------------------- a3 combine
+constexpr int kCombBatch = 32;
 // Block per query row, 128 threads, 4 consecutive columns per thread per pass.
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
@@ -120,8 +157,16 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
                                                       int width) {
   const size_t row = blockIdx.x;
   const float* lp = lse_part + row * S;
+  __shared__ float red[2][4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;   // 128 threads = 2 waves
+  // row maximum and sum of the chunk weights, every thread taking splits t, t + 128, ...
   float m = -INFINITY;
-  for (int u = 0; u < S; ++u) m = fmaxf(m, lp[u]);
+  for (int u = threadIdx.x; u < S; u += blockDim.x) m = fmaxf(m, lp[u]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if (lane == 0) red[0][wv] = m;
+  __syncthreads();
+  m = fmaxf(red[0][0], red[0][1]);
   if (m == -INFINITY) {
     for (int c = threadIdx.x; c < width; c += blockDim.x) o[row * width + c] = 0.f;
     if (threadIdx.x == 0 && lse) lse[row] = -INFINITY;
@@ -129,22 +174,34 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   }
   const float ml = m * kLog2e;
   float tot = 0.f;
-  for (int u = 0; u < S; ++u) tot += exp2f(fmaf(lp[u], kLog2e, -ml));
+  for (int u = threadIdx.x; u < S; u += blockDim.x) tot += exp2f(fmaf(lp[u], kLog2e, -ml));
+  tot = wave_sum(tot);
+  if (lane == 0) red[1][wv] = tot;
+  __syncthreads();
+  tot = red[1][0] + red[1][1];
   const float inv = 1.f / tot;
   const float* op = o_part + row * S * width;
   for (int c = 4 * threadIdx.x; c < width; c += 4 * blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    // loads are unconditional so that 16 of them can be in flight; an empty split
-    // (lse -inf, weight 0) may hold anything, so its values are selected away, not scaled
-#pragma unroll 16
-    for (int u = 0; u < S; ++u) {
-      const float wgt = exp2f(fmaf(lp[u], kLog2e, -ml));
-      const float4 v = *reinterpret_cast<const float4*>(op + static_cast<size_t>(u) * width + c);
-      const bool use = wgt > 0.f;
-      acc.x = fmaf(wgt, use ? v.x : 0.f, acc.x);
-      acc.y = fmaf(wgt, use ? v.y : 0.f, acc.y);
-      acc.z = fmaf(wgt, use ? v.z : 0.f, acc.z);
-      acc.w = fmaf(wgt, use ? v.w : 0.f, acc.w);
+    // splits in batches of kCombBatch whose loads are all issued before any is used; an
+    // empty split (lse -inf, weight 0) may hold anything, so its values are selected
+    // away, not scaled
+    for (int u0 = 0; u0 < S; u0 += kCombBatch) {
+      float4 v[kCombBatch];
+#pragma unroll
+      for (int b = 0; b < kCombBatch; ++b)
+        if (u0 + b < S)
+          v[b] = *reinterpret_cast<const float4*>(op + static_cast<size_t>(u0 + b) * width + c);
+#pragma unroll
+      for (int b = 0; b < kCombBatch; ++b) {
+        if (u0 + b >= S) break;
+        const float wgt = exp2f(fmaf(lp[u0 + b], kLog2e, -ml));
+        const bool use = wgt > 0.f;
+        acc.x = fmaf(wgt, use ? v[b].x : 0.f, acc.x);
+        acc.y = fmaf(wgt, use ? v[b].y : 0.f, acc.y);
+        acc.z = fmaf(wgt, use ? v[b].z : 0.f, acc.z);
+        acc.w = fmaf(wgt, use ? v[b].w : 0.f, acc.w);
+      }
     }
     *reinterpret_cast<float4*>(o + row * width + c) =
         make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
@@ -157,6 +214,8 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
 // read W_UV row v0 + 8 wave + r in 128-byte segments (8 elements a lane); the queries'
 // latent outputs sit in LDS.  The 8 lanes of a row meet by shuffles.
 constexpr int kUvRows = 32;
+constexpr int kUvBatch = 8;   // weight chunks per thread in flight at once
+constexpr int kUvStage = 4;   // o_lat float4 loads per thread in flight at once
 template <typename T>
 __global__ __launch_bounds__(256) void out_uv_kernel(const float* __restrict__ o_lat,
                                                      const T* __restrict__ w_uv,
@@ -167,12 +226,23 @@ __global__ __launch_bounds__(256) void out_uv_kernel(const float* __restrict__ o
   const int w = h / (H / Hw);
   const int nq = min(kQB, NQ - q0);
   const int tid = threadIdx.x;
-  for (int idx = 4 * tid; idx < kQB * d_c; idx += 4 * blockDim.x) {
-    const int jq = idx / d_c, c = idx - jq * d_c;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (jq < nq)
-      v = *reinterpret_cast<const float4*>(o_lat + (static_cast<size_t>(q0 + jq) * H + h) * d_c + c);
-    *reinterpret_cast<float4*>(&os[idx]) = v;
+  // the queries' latent outputs: up to kUvStage float4 loads per thread in flight at once
+  for (int i0 = 4 * tid; i0 < kQB * d_c; i0 += 4 * blockDim.x * kUvStage) {
+    float4 v[kUvStage];
+#pragma unroll
+    for (int b = 0; b < kUvStage; ++b) {
+      const int idx = i0 + 4 * blockDim.x * b;
+      const int jq = idx / d_c, c = idx - jq * d_c;
+      v[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (idx < kQB * d_c && jq < nq)
+        v[b] = *reinterpret_cast<const float4*>(
+            o_lat + (static_cast<size_t>(q0 + jq) * H + h) * d_c + c);
+    }
+#pragma unroll
+    for (int b = 0; b < kUvStage; ++b) {
+      const int idx = i0 + 4 * blockDim.x * b;
+      if (idx < kQB * d_c) *reinterpret_cast<float4*>(&os[idx]) = v[b];
+    }
   }
   __syncthreads();
   const int lane = tid & 63, wave = tid >> 6;
@@ -182,10 +252,18 @@ __global__ __launch_bounds__(256) void out_uv_kernel(const float* __restrict__ o
   for (int jq = 0; jq < kQB; ++jq) acc[jq] = 0.f;
   if (v < d_v) {
     const T* wr = w_uv + (static_cast<size_t>(w) * d_v + v) * d_c;
-#pragma unroll 8
-    for (int c = 8 * cg; c < d_c; c += 64) {
+    // columns 8 cg + 64 b in batches of kUvBatch, loads issued before use
+    for (int c0 = 8 * cg; c0 < d_c; c0 += 64 * kUvBatch) {
+     Raw8<T> raw[kUvBatch];
+#pragma unroll
+     for (int bt = 0; bt < kUvBatch; ++bt)
+       if (c0 + 64 * bt < d_c) raw[bt] = load_raw8(wr + c0 + 64 * bt);
+#pragma unroll
+     for (int bt = 0; bt < kUvBatch; ++bt) {
+      const int c = c0 + 64 * bt;
+      if (c >= d_c) break;
       float wv[8];
-      load8(wr + c, wv);
+      to_f32(raw[bt], wv);
 #pragma unroll
       for (int jq = 0; jq < kQB; ++jq) {
         const float4 a = *reinterpret_cast<const float4*>(&os[jq * d_c + c]);
@@ -197,6 +275,7 @@ __global__ __launch_bounds__(256) void out_uv_kernel(const float* __restrict__ o
         t = fmaf(b.z, wv[6], t); t = fmaf(b.w, wv[7], t);
         acc[jq] = t;
       }
+     }
     }
   }
 #pragma unroll
@@ -209,6 +288,64 @@ __global__ __launch_bounds__(256) void out_uv_kernel(const float* __restrict__ o
   }
   if (v < d_v && cg == 0) {
     for (int jq = 0; jq < nq; ++jq) out[(static_cast<size_t>(q0 + jq) * H + h) * d_v + v] = acc[jq];
+  }
+}
+
+// a4 on the matrix cores (bf16 weights): out^T[v][n] = sum_c W_UV[w(h)][v][c] o[n][h][c] as
+// v_mfma_f32_32x32x16_bf16 with the weight rows as the A operand (v = M, c = K, both in
+// their natural row-major layout) and the latent outputs, rounded to bf16, as the B
+// operand (query = N, padded to 32).  One wave per (head, 32 value rows); query blocks
+// of 32 in turn.  Loads run kUvmSteps K-steps ahead of their MFMAs.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+constexpr int kUvmSteps = 8;
+
+__global__ __launch_bounds__(64) void out_uv_mfma_kernel(const float* __restrict__ o_lat,
+                                                         const bf16_t* __restrict__ w_uv,
+                                                         float* __restrict__ out, int NQ,
+                                                         int H, int Hw, int d_c, int d_v) {
+  const int h = blockIdx.x, v0 = 32 * blockIdx.y;
+  const int w = h / (H / Hw);
+  const int lane = threadIdx.x, m = lane & 31, g = lane >> 5;
+  const int n_k = d_c / 16;
+  const int v = min(v0 + m, d_v - 1);   // rows past d_v read a valid row, never stored
+  const bf16_t* wr = w_uv + (static_cast<size_t>(w) * d_v + v) * d_c + 8 * g;
+  for (int n0 = 0; n0 < NQ; n0 += 32) {
+    const int n = n0 + m;
+    const float* orow = o_lat + (static_cast<size_t>(min(n, NQ - 1)) * H + h) * d_c + 8 * g;
+    f32x16_t acc = {};
+    for (int k0 = 0; k0 < n_k; k0 += kUvmSteps) {
+      uint4 a[kUvmSteps];
+      float4 b[kUvmSteps][2];
+#pragma unroll
+      for (int t = 0; t < kUvmSteps; ++t) {
+        const int ks = min(k0 + t, n_k - 1);
+        a[t] = *reinterpret_cast<const uint4*>(wr + 16 * ks);
+        b[t][0] = *reinterpret_cast<const float4*>(orow + 16 * ks);
+        b[t][1] = *reinterpret_cast<const float4*>(orow + 16 * ks + 4);
+      }
+#pragma unroll
+      for (int t = 0; t < kUvmSteps; ++t) {
+        if (k0 + t >= n_k) break;
+        bf16x8_t bv;
+        bv[0] = static_cast<__bf16>(b[t][0].x); bv[1] = static_cast<__bf16>(b[t][0].y);
+        bv[2] = static_cast<__bf16>(b[t][0].z); bv[3] = static_cast<__bf16>(b[t][0].w);
+        bv[4] = static_cast<__bf16>(b[t][1].x); bv[5] = static_cast<__bf16>(b[t][1].y);
+        bv[6] = static_cast<__bf16>(b[t][1].z); bv[7] = static_cast<__bf16>(b[t][1].w);
+        if (n >= NQ) bv = bf16x8_t{};
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[t]), bv,
+                                                      acc, 0, 0, 0);
+      }
+    }
+    // lane (query n, half g) holds value rows 8 (j / 4) + 4 g + j % 4 of the block
+    if (n < NQ) {
+      float* orow_out = out + (static_cast<size_t>(n) * H + h) * d_v + v0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int vv = 8 * (j >> 2) + 4 * g + (j & 3);
+        if (v0 + vv < d_v) orow_out[vv] = acc[j];
+      }
+    }
   }
 }
 
@@ -328,6 +465,10 @@ hipError_t launch_out_uv(const mla_shape_t& s, const float* o_lat, const void* w
     hipLaunchKernelGGL(out_uv_kernel<float>, grid, dim3(256), lds, st, o_lat,
                        static_cast<const float*>(w_uv), out, NQ, s.n_heads, s.n_wheads,
                        s.d_c, s.d_v);
+  else if (s.d_c % 16 == 0)
+    hipLaunchKernelGGL(out_uv_mfma_kernel, dim3(s.n_heads, (s.d_v + 31) / 32), dim3(64), 0,
+                       st, o_lat, static_cast<const bf16_t*>(w_uv), out, NQ, s.n_heads,
+                       s.n_wheads, s.d_c, s.d_v);
   else
     hipLaunchKernelGGL(out_uv_kernel<bf16_t>, grid, dim3(256), lds, st, o_lat,
                        static_cast<const bf16_t*>(w_uv), out, NQ, s.n_heads, s.n_wheads,
