@@ -8,34 +8,26 @@
 // query the keys are never decompressed; AI Radio episode on GQLA, "Key concepts": on
 // the MQA-absorb path the latent is the shared key and value).
 //
-// Two kernels, both one workgroup per (sequence b, chunk u, block of query rows), rows
-// being the flattened (s, h) pairs, and both using v_mfma_f32_32x32x16_bf16 for the two
-// contractions: S^T[token][row] = C_tile . q_abs^T over the 576-wide row, and
-// O^T[latent][row] += C_tile^T . P^T over the tile's 32 tokens.
-//
-// Ring kernel (rows a multiple of 64; 256 threads, one workgroup per CU):
-//  * The chunk streams through a 4-deep LDS ring of 32-token tiles (36 KB each), filled
-//    two tiles ahead by global_load_lds_dwordx4 (HBM -> LDS, no register staging).  All
-//    four waves issue a quarter of every tile's loads; rows land XOR-swizzled by 16-byte
-//    chunk so both the row-wise and the transposed reads are free of bank conflicts.
-//  * Waves 0 and 1 are score waves (32 rows each, q_abs held in registers as the B
-//    operand); they compute tile k's scores, run the softmax and publish P (bf16).
-//  * Waves 2 and 3 are value waves (256 latent columns each, O^T in 256 AGPRs); they
-//    consume tile k-1, reading it transposed with ds_read_b64_tr_b16.
-//  * One workgroup barrier per tile.  The softmax keeps a lazy per-row reference: it
-//    only moves when a score exceeds it by more than a slack of 32 (log2 units), so P
-//    stays below 2^32 and the accumulators never need rescaling; when a reference must
-//    move, the whole chunk is rerun from its first tile with the raised reference (rare:
-//    each rerun strictly raises a reference, at most n_tiles reruns).
-//  * The two 64-row blocks of one (b, u) are 8 workgroups apart in the grid so that they
-//    run on the same XCD and the second one's tile reads hit its L2.
-// Rows32 kernel (rows a multiple of 32, e.g. 32 GQLA heads at s_q = 1): one score wave
-// loads cache rows straight into A-operand registers and stages the latent columns for
-// one value wave through a double-buffered LDS tile, same softmax scheme.
-//
-// Rows past a sequence's end in its last page are never used: their loads are clamped to
-// the tile's first row (a valid token) and their scores masked, so NaN padding cannot
-// reach the output.
+// One kernel, templated on NQ (1 or 2 score waves, i.e. 32 or 64 query rows per
+// workgroup; rows are the flattened (s, h) pairs).  One workgroup per (sequence b, chunk
+// u, row block), one per CU (~160 KB of LDS), NQ + 2 waves.  Both contractions run as
+// v_mfma_f32_32x32x16_bf16: S^T[token][row] = C_tile . q_abs^T over the 576-wide row, and
+// O^T[latent][row] += C_tile^T . P^T over the tile's 32 tokens.  Per 32-token tile ("slot"
+// s, one workgroup barrier each):
+//  * The two value waves stream the chunk through a 4-deep LDS ring: each loads half of
+//    tile s+2 into registers during slot s (buffer loads; the buffer's size is the tile's
+//    valid rows, so rows past the chunk end read as zeros) and stores it at the start of
+//    slot s+1.  They then multiply tile s-2, reading it transposed with ds_read_b64_tr_b16
+//    as the A operand; O^T lives in AGPRs (256 latent columns x 32 NQ rows per wave).
+//  * The score waves (32 rows each, q_abs held in registers as the B operand) issue the 36
+//    MFMAs of tile s and, between them, the softmax of tile s-1 in small pieces that issue
+//    while the matrix core is busy; P (bf16) goes to LDS for the value waves.
+//  * The softmax keeps a lazy per-row reference: it only moves when a score exceeds it by
+//    more than a slack of 32 (log2 units), so P stays below 2^32 and the accumulators
+//    never need rescaling; when a reference must move, the chunk is rerun from its first
+//    tile with the raised reference (rare: each rerun strictly raises a reference).
+//  * The row blocks of one (b, u) are 8 workgroups apart in the grid so that they run on
+//    the same XCD and share its L2.
 #include <math.h>
 #include <stdlib.h>
 
@@ -49,7 +41,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -60,34 +51,6 @@ constexpr int kPage = 64;      // tokens per page
 constexpr int kTT = 32;        // tokens per tile
 constexpr int kKS = kD / 16;   // 36 K-steps of 16 in the score contraction
 constexpr int kPRow = 40;      // P row stride in LDS (bf16): 80 B, conflict-free b128 reads
-
-// XOR swizzle of the 16-byte chunk index inside a latent tile row (64 chunks per row):
-// 8 consecutive tokens hit 8 distinct chunks (conflict-free b128 writes) and any 4
-// consecutive tokens aligned to 4 put a given 32-byte pair on 4 distinct bank groups
-// (conflict-free transposed reads).
-__device__ __forceinline__ int swz(int tok) { return ((tok & 3) << 1) | ((tok >> 2) & 1); }
-
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt and lgkmcnt left at their "no wait" maxima).  The builtin, unlike inline
-// asm, is seen by the compiler's own wait insertion, which then adds no redundant waits.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
-}
-
-__device__ __forceinline__ bf16x8 load_row_chunk(const bf16_t* p) {
-  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-template <int NQ>
-struct Smem {
-  bf16_t cbuf[2][kTT * kDC];       // latent tile (swizzled rows), double buffered
-  bf16_t pbuf[2][32 * NQ * kPRow];  // P[row][token] (bf16), double buffered
-  float lfin[32 * NQ];              // final row sums
-  int restart;                      // set by a score wave when a reference must move
-};
 
 struct Work {
   const bf16_t* q_abs;
@@ -101,301 +64,6 @@ struct Work {
   float slack;          // lazy-reference slack (log2 units)
 };
 
-// After the barrier that ends a slot every wave reads the restart flag; if it is set,
-// all waves meet twice more (everyone has read it / it has been cleared) and rerun the
-// chunk.  Every wave takes the same path, so barrier counts stay equal.
-template <typename SM>
-__device__ __forceinline__ bool check_restart(SM& sm) {
-  const bool r = __builtin_amdgcn_readfirstlane(sm.restart) != 0;
-  if (r) {
-    __syncthreads();
-    if (threadIdx.x == 0) sm.restart = 0;
-    __syncthreads();
-  }
-  return r;
-}
-
-// Score wave QW: rows [32 QW, 32 QW + 32) of the workgroup.
-template <int NQ, int QW>
-__device__ __forceinline__ void score_role(Smem<NQ>& sm, const Work& w, int lane) {
-  constexpr int KS_OWN = 32 / NQ;   // latent K-steps this wave stages for the value waves
-  const int n32 = lane & 31, g = lane >> 5;
-  bf16x8 qreg[kKS];                 // B operand: q_abs[row n32][16 ks + 8 g .. +8]
-  bf16x8 rreg[kKS];                 // A operand: cache row (token n32)[16 ks + 8 g .. +8]
-  float m_run = -INFINITY, l_run = 0.f;
-  const int r = w.y * 32 * NQ + 32 * QW + n32;     // row within the sequence: s*H + h
-  const int top_row = min(w.hi, w.T - w.s_q + r / w.H + 1);
-  // A 32-token tile never straddles a page (chunks start on page boundaries), so its
-  // page is wave-uniform and comes from a scalar load; rows past the chunk end are
-  // clamped to the tile's first row.
-  auto tile_page = [&](int k) -> int {
-    return w.ptb[__builtin_amdgcn_readfirstlane(w.lo + k * kTT) >> 6];
-  };
-  auto tile_row_ptr = [&](int k, int page) -> const bf16_t* {
-    const int t0 = __builtin_amdgcn_readfirstlane(w.lo + k * kTT);
-    const int row = (t0 & (kPage - 1)) + ((t0 + n32 < w.hi) ? n32 : 0);
-    return w.pool + (static_cast<size_t>(page) * kPage + row) * kD + 8 * g;
-  };
-  const bf16_t* qp = w.q_abs + (w.qrow0 + 32 * QW + n32) * kD + 8 * g;
-#pragma unroll
-  for (int ks = 0; ks < kKS; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
-  const int sw = swz(n32);
-  int cw[4];                          // byte offset of chunk 2b+g in a row, swizzled
-#pragma unroll
-  for (int b4 = 0; b4 < 4; ++b4) cw[b4] = 16 * ((2 * b4 + g) ^ sw);
-
-  bool again = true;
-  int reruns = 0;   // each rerun passes its triggering tile, so at most n_tiles happen
-  while (again) {
-    again = false;
-    l_run = 0.f;
-    int page_next = 0;    // page of tile k+1, loaded one tile ahead
-    if (w.n_tiles > 0) {
-      const bf16_t* rp = tile_row_ptr(0, tile_page(0));
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) rreg[ks] = load_row_chunk(rp + 16 * ks);
-      page_next = tile_page(min(1, w.n_tiles - 1));
-    }
-    for (int k = 0; k <= w.n_tiles; ++k) {
-      if (k < w.n_tiles) {
-        const int bi = k & 1;
-        // the last tile re-fetches itself, which keeps the load stream branch-free
-        const int kn = min(k + 1, w.n_tiles - 1);
-        const bf16_t* np = tile_row_ptr(kn, page_next);
-        page_next = tile_page(min(k + 2, w.n_tiles - 1));
-        char* crow = reinterpret_cast<char*>(&sm.cbuf[bi][n32 * kDC]);
-        f32x16 sacc;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks) {
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rreg[ks], qreg[ks], sacc, 0, 0, 0);
-          if (ks >= QW * KS_OWN && ks < (QW + 1) * KS_OWN)
-            // chunk 2ks+g = 8(ks/4) + (2(ks%4)+g): the swizzle only touches the low part
-            *reinterpret_cast<bf16x8*>(crow + cw[ks & 3] + 128 * (ks >> 2)) = rreg[ks];
-          rreg[ks] = load_row_chunk(np + 16 * ks);
-        }
-        // online softmax on S^T: lane holds row n32, tokens 8(j/4) + 4g + (j%4)
-        const int t0 = w.lo + k * kTT + 4 * g;
-        float z[16];
-        float mt = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int t = t0 + 8 * (j >> 2) + (j & 3);
-          z[j] = (t < top_row) ? sacc[j] * w.zscale : -INFINITY;
-          mt = fmaxf(mt, z[j]);
-        }
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        // First visible tile of a row: take its maximum as the reference (nothing has
-        // been accumulated for the row yet).  Later, a score more than `slack` above the
-        // reference moves it and reruns the whole chunk (rare).
-        const bool move = m_run != -INFINITY && mt > m_run + w.slack;
-        if (m_run == -INFINITY || move) m_run = mt;
-        if (__builtin_amdgcn_ballot_w64(move) && reruns <= w.n_tiles) sm.restart = 1;
-        const bool live = m_run != -INFINITY;
-        bf16_t* prow = &sm.pbuf[bi][(32 * QW + n32) * kPRow];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          i16x4 pk;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = live ? exp2f(z[4 * a + i] - m_run) : 0.f;
-            l_run += p;
-            pk[i] = __builtin_bit_cast(short, static_cast<__bf16>(p));
-          }
-          *reinterpret_cast<i16x4*>(prow + 8 * a + 4 * g) = pk;
-        }
-      }
-      __syncthreads();
-      if (check_restart(sm)) {
-        again = true;
-        ++reruns;
-        break;
-      }
-    }
-  }
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (g == 0) {
-    sm.lfin[32 * QW + n32] = l_tot;
-    const size_t orow = (w.qrow0 + 32 * QW + n32) * w.S + w.u;
-    w.lse_part[orow] = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();
-}
-
-// One value-wave tile: acc[mb][nb] (+)= C^T[latent block mb][tile] . P^T[tile][rows nb].
-// FIRST starts the accumulators from zero, so every definition of them is an MFMA.
-template <int NQ, int MB, bool FIRST>
-__device__ __forceinline__ void value_tile(Smem<NQ>& sm, int bi, const int (&trofs)[2][2][2],
-                                           int n32, int g, f32x16 (&acc)[MB][NQ]) {
-  // B operand: P^T[token 16 kt + 8 g + i][row 32 nb + n32]
-  bf16x8 pb[2][NQ];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int nb = 0; nb < NQ; ++nb)
-      pb[kt][nb] = *reinterpret_cast<const bf16x8*>(
-          &sm.pbuf[bi][(32 * nb + n32) * kPRow + 16 * kt + 8 * g]);
-  const char* cb = reinterpret_cast<const char*>(&sm.cbuf[bi][0]);
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      // A operand: C^T[latent][token] by transposed LDS reads; 16-lane group q16 gets
-      // latent rows m_base + i and tokens 16 kt + 8 g16 + (0..7).  Block mb adds
-      // 128 * (mb / 2) bytes: chunk + 8 leaves the swizzled bits alone.
-      const int ofs = 128 * (mb >> 1);
-      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(const __attribute__((address_space(3))) char*)(
-              cb + trofs[mb & 1][kt][0] + ofs));
-      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(const __attribute__((address_space(3))) char*)(
-              cb + trofs[mb & 1][kt][1] + ofs));
-      const i16x8 a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
-#pragma unroll
-      for (int nb = 0; nb < NQ; ++nb) {
-        if (FIRST && kt == 0) {
-          const f32x16 zero = {};
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kt][nb], zero, 0, 0, 0);
-        } else {
-          acc[mb][nb] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kt][nb], acc[mb][nb], 0, 0, 0);
-        }
-      }
-    }
-  }
-}
-
-// Value wave VW: latent columns [VW * 512/NQ, (VW+1) * 512/NQ) for all 32*NQ rows.
-template <int NQ>
-__device__ __forceinline__ void value_role(Smem<NQ>& sm, const Work& w, int vw, int lane) {
-  constexpr int LAT_PV = kDC / NQ;  // latent columns per value wave
-  constexpr int MB = LAT_PV / 32;   // 32-wide M blocks
-  const int n32 = lane & 31, g = lane >> 5;
-  const int lat0 = vw * LAT_PV;
-  const int q16 = lane >> 4, L = lane & 15;
-  const int m_base = 16 * (q16 & 1), g16 = q16 >> 1;
-  // byte offsets of this lane's transposed-read chunks for M blocks 0/1, both K-steps
-  // and both token quartets
-  int trofs[2][2][2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par)
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int h4 = 0; h4 < 2; ++h4) {
-        const int col = lat0 + 32 * par + m_base + 4 * (L & 3);
-        const int tok = 16 * kt + 8 * g16 + 4 * h4 + (L >> 2);
-        trofs[par][kt][h4] = tok * (kDC * 2) + (((col >> 3) ^ swz(tok)) * 16) + (col & 7) * 2;
-      }
-  while (true) {
-    // slot 0: the score waves compute tile 0
-    __syncthreads();
-    if (check_restart(sm)) continue;
-    if (w.n_tiles == 0) {
-      __syncthreads();   // the score waves have published the row sums
-      float* orow0 = w.o_part + (w.qrow0 * w.S + w.u) * kDC + lat0 + 4 * g;
-      for (int nb = 0; nb < NQ; ++nb)
-        for (int c = 0; c < LAT_PV; c += 8)
-          *reinterpret_cast<float4*>(orow0 + (32 * nb + n32) * w.S * kDC + c) =
-              make_float4(0.f, 0.f, 0.f, 0.f);
-      return;
-    }
-    // slot 1: tile 0, accumulators start from zero
-    f32x16 acc[MB][NQ];
-    value_tile<NQ, MB, true>(sm, 0, trofs, n32, g, acc);
-    __syncthreads();
-    if (check_restart(sm)) continue;
-    bool restarted = false;
-    for (int k = 2; k <= w.n_tiles; ++k) {
-      value_tile<NQ, MB, false>(sm, (k - 1) & 1, trofs, n32, g, acc);
-      __syncthreads();
-      if (check_restart(sm)) {
-        restarted = true;
-        break;
-      }
-    }
-    if (restarted) continue;
-    __syncthreads();   // the score waves have published the row sums
-#pragma unroll
-    for (int nb = 0; nb < NQ; ++nb) {
-      const float l = sm.lfin[32 * nb + n32];
-      const float inv = (l > 0.f) ? 1.f / l : 0.f;
-      float* orow = w.o_part + ((w.qrow0 + 32 * nb + n32) * w.S + w.u) * kDC + lat0 + 4 * g;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          float4 v;
-          v.x = acc[mb][nb][4 * a + 0] * inv;
-          v.y = acc[mb][nb][4 * a + 1] * inv;
-          v.z = acc[mb][nb][4 * a + 2] * inv;
-          v.w = acc[mb][nb][4 * a + 3] * inv;
-          *reinterpret_cast<float4*>(orow + 32 * mb + 8 * a) = v;
-        }
-    }
-    return;
-  }
-}
-
-template <int NQ>
-__global__ __launch_bounds__(128 * NQ, 1) void decode_absorbed_mfma_rows32_kernel(
-    const bf16_t* __restrict__ q_abs, const bf16_t* __restrict__ pool,
-    const int32_t* __restrict__ pt, const int32_t* __restrict__ lens,
-    float* __restrict__ o_part, float* __restrict__ lse_part, int s_q, int H, int max_pages,
-    int S, int split_tokens, float zscale, float slack, int n_units, int n_yblk) {
-  __shared__ __attribute__((aligned(16))) Smem<NQ> sm;
-  const int wg = blockIdx.x;
-  const int rest = wg >> 3;
-  const int y = rest % n_yblk;
-  const int unit = (rest / n_yblk) * 8 + (wg & 7);
-  if (unit >= n_units) return;  // uniform for the whole workgroup, before any barrier
-  Work w;
-  const int b = unit / S;
-  w.u = unit - b * S;
-  w.T = lens[b];
-  split_range(w.T, w.u, S, kPage, split_tokens, w.lo, w.hi);
-  w.n_tiles = (w.hi > w.lo) ? (w.hi - w.lo + kTT - 1) / kTT : 0;
-  w.q_abs = q_abs;
-  w.pool = pool;
-  w.ptb = pt + static_cast<size_t>(b) * max_pages;
-  w.o_part = o_part;
-  w.lse_part = lse_part;
-  w.qrow0 = static_cast<size_t>(b) * s_q * H + static_cast<size_t>(y) * 32 * NQ;
-  w.s_q = s_q;
-  w.H = H;
-  w.y = y;
-  w.S = S;
-  w.zscale = zscale;
-  w.slack = slack;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (threadIdx.x == 0) sm.restart = 0;
-  __syncthreads();
-  if (wave == 0)
-    score_role<NQ, 0>(sm, w, lane);
-  else if (NQ == 2 && wave == 1)
-    score_role<NQ, (NQ == 2 ? 1 : 0)>(sm, w, lane);
-  else
-    value_role<NQ>(sm, w, wave - NQ, lane);
-}
-
-
-// ====================================================================================
-// 64-row kernel: latent tiles staged through a 4-tile LDS ring by direct-to-LDS loads.
-//
-// Every wave issues 9 of a 32-token tile's 36 wave-wide global_load_lds_dwordx4
-// instructions (1 KB contiguous each, so the vector memory path moves whole cache lines),
-// two tiles ahead of use.  They are issued from inline asm: the compiler then does not
-// treat them as LDS stores in flight, so it adds no waits of its own before ring reads;
-// instead every wave waits for its own loads of the next tile (vmcnt) before the slot's
-// barrier.  A DMA load has no destination registers, so nothing in flight can overwrite
-// a register.  The ring keeps raw cache rows with 16-byte chunks XOR-swizzled within
-// groups of 8 per row; the score waves' 128-bit operand reads and the value waves'
-// transposed reads are bank-conflict free on it.  Score waves (rows 0-31 and 32-63) read
-// their A operand from the ring and hold only q_abs in registers; the value waves read
-// the latent columns of the same tile one slot later.
-// ====================================================================================
 namespace ring {
 
 constexpr int kRowB = kD * 2;              // 1152 bytes per cache row
@@ -506,42 +174,6 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <bool MASK>
-__device__ __forceinline__ void softmax_tile(const f32x16& sacc, int lim, float zscale,
-                                             float slack, float& m_ref, float& l_run,
-                                             bool& move, bf16_t* prow, int g) {
-  // lane holds tokens 8(j/4) + 4g + (j%4) of the tile for its row; lim = visible count
-  float mx = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const bool vis = !MASK || (8 * (j >> 2) + 4 * g + (j & 3) < lim);
-    mx = fmaxf(mx, vis ? sacc[j] : -INFINITY);
-  }
-  const float mt = xhalf_max(mx * zscale);
-  // First visible tile of a row fixes its reference; a later jump beyond the slack
-  // raises it to this tile's maximum and reruns the chunk, so the rerun cannot trigger
-  // again at this tile: every rerun strictly raises some row's reference.
-  move = m_ref != -INFINITY && mt > m_ref + slack;
-  if (m_ref == -INFINITY || move) m_ref = mt;
-  const bool live = m_ref != -INFINITY;
-  const float nm = -m_ref;
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 4 * a + i;
-      const bool vis = !MASK || (8 * a + 4 * g + i < lim);
-      p[i] = (live && vis) ? __builtin_amdgcn_exp2f(fmaf(sacc[j], zscale, nm)) : 0.f;
-      l_run += p[i];
-    }
-    i16x4 pk;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pk[i] = __builtin_bit_cast(short, static_cast<__bf16>(p[i]));
-    *reinterpret_cast<i16x4*>(prow + 8 * a + 4 * g) = pk;
-  }
-}
-
 // One score-wave slot: the 36 MFMAs of S^T for the tile at `tb` (into sacc_out) and the
 // softmax of the previous tile's scores (sacc_in).  The softmax is cut into pieces of a
 // few VALU instructions that sit between consecutive MFMAs, where they issue while the
@@ -628,11 +260,11 @@ __device__ __forceinline__ void score_slot(const char* tb, const bf16x8 (&qreg)[
 
 // Score wave QW (rows 32 QW .. 32 QW + 31).  Slot s: the MFMAs of tile s and the softmax
 // (P, published to LDS) of tile s-1, so the value waves use tile s-2.
-template <int QW>
+template <int NQ, int QW>
 __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
   const int n32 = lane & 31, g = lane >> 5;
   bf16x8 qreg[kKS];
-  const int r = w.y * 64 + 32 * QW + n32;
+  const int r = w.y * 32 * NQ + 32 * QW + n32;
   const int top_row = min(w.hi, w.T - w.s_q + r / w.H + 1);
   const bf16_t* qp = w.q_abs + (w.qrow0 + 32 * QW + n32) * kD + 8 * g;
 #pragma unroll
@@ -698,15 +330,15 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
 
 // One value-wave tile from ring slot `slot`: acc (+)= C^T . P^T.  The transposed
 // A-operand reads run four (mb, kt) steps ahead of their MFMA pair.
-template <bool FIRST>
+template <int NQ, bool FIRST>
 __device__ __forceinline__ void value_ring_tile(Smem& sm, int slot, int pb_i,
                                                 const int (&trofs)[2][2][2], int n32, int g,
-                                                f32x16 (&acc)[8][2]) {
-  bf16x8 pb[2][2];
+                                                f32x16 (&acc)[8][NQ]) {
+  bf16x8 pb[2][NQ];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < NQ; ++nb)
       pb[kt][nb] = *reinterpret_cast<const bf16x8*>(
           &sm.pbuf[pb_i][(32 * nb + n32) * kPRow + 16 * kt + 8 * g]);
   const char* cb = &sm.ring[slot][0];
@@ -741,7 +373,7 @@ __device__ __forceinline__ void value_ring_tile(Smem& sm, int slot, int pb_i,
   for (int st = 0; st < kSteps; ++st) {
     const int mb = st >> 1, kt = st & 1;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NQ; ++nb) {
       if (FIRST && kt == 0) {
         const f32x16 zero = {};
         acc[mb][nb] =
@@ -759,11 +391,10 @@ __device__ __forceinline__ void value_ring_tile(Smem& sm, int slot, int pb_i,
 
 // Value wave VW: latent columns [256 VW, 256 VW + 256) for all 64 rows.  Slot k: its
 // share of tile k+2's loads, then the value product of tile k-1.
-template <int VW>
+template <int NQ, int VW>
 __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
   const int n32 = lane & 31, g = lane >> 5;
   constexpr int lat0 = VW * 256;
-  constexpr int wave = 2 + VW;
   const int q16 = lane >> 4, L = lane & 15;
   const int m_base = 16 * (q16 & 1), g16 = q16 >> 1;
   int trofs[2][2][2];
@@ -807,20 +438,20 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
     if (n == 0) {
       __syncthreads();   // the score waves have published the row sums
       float* orow0 = w.o_part + (w.qrow0 * w.S + w.u) * kDC + lat0 + 4 * g;
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NQ; ++nb)
         for (int c = 0; c < 256; c += 8)
           *reinterpret_cast<float4*>(orow0 + (32 * nb + n32) * w.S * kDC + c) =
               make_float4(0.f, 0.f, 0.f, 0.f);
       return;
     }
     // slot 2 (peeled, so the accumulators are first written outside the loop)
-    f32x16 acc[8][2];
+    f32x16 acc[8][NQ];
     long long seen = sm.flag[0];
     store_stage(sm, stg, lane, 3, VW, 2);
     __builtin_amdgcn_sched_barrier(0);
     load_stage(stg, plan, w, min(4, last), lane);
     __builtin_amdgcn_sched_barrier(0);
-    value_ring_tile<true>(sm, 0, 0, trofs, n32, g, acc);
+    value_ring_tile<NQ, true>(sm, 0, 0, trofs, n32, g, acc);
     bool restarted = seen == rerun_tag(reruns, 0);
     __syncthreads();
     for (int s = 3; s <= n + 1 && !restarted; ++s) {
@@ -829,7 +460,7 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
       __builtin_amdgcn_sched_barrier(0);
       load_stage(stg, plan, w, min(s + 2, last), lane);
       __builtin_amdgcn_sched_barrier(0);
-      value_ring_tile<false>(sm, (s - 2) & (kNB - 1), (s - 2) & 1, trofs, n32, g, acc);
+      value_ring_tile<NQ, false>(sm, (s - 2) & (kNB - 1), (s - 2) & 1, trofs, n32, g, acc);
       restarted = seen == rerun_tag(reruns, s - 2);
       __syncthreads();
     }
@@ -839,7 +470,7 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
     }
     __syncthreads();   // the score waves have published the row sums
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NQ; ++nb) {
       const float l = sm.lfin[32 * nb + n32];
       const float inv = (l > 0.f) ? 1.f / l : 0.f;
       float* orow = w.o_part + ((w.qrow0 + 32 * nb + n32) * w.S + w.u) * kDC + lat0 + 4 * g;
@@ -865,7 +496,8 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
 
 // One workgroup per CU (the ring takes 158 KB of LDS), so the scheduler may use the
 // whole register file of each SIMD for operand prefetch.
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int NQ>
+__global__ __launch_bounds__(64 * (NQ + 2), 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_absorbed_mfma_ring_kernel(
     const bf16_t* __restrict__ q_abs, const bf16_t* __restrict__ pool,
     const int32_t* __restrict__ pt, const int32_t* __restrict__ lens,
@@ -888,7 +520,7 @@ void decode_absorbed_mfma_ring_kernel(
   w.ptb = pt + static_cast<size_t>(b) * max_pages;
   w.o_part = o_part;
   w.lse_part = lse_part;
-  w.qrow0 = static_cast<size_t>(b) * s_q * H + static_cast<size_t>(y) * 64;
+  w.qrow0 = static_cast<size_t>(b) * s_q * H + static_cast<size_t>(y) * 32 * NQ;
   w.s_q = s_q;
   w.H = H;
   w.y = y;
@@ -898,14 +530,15 @@ void decode_absorbed_mfma_ring_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (threadIdx.x == 0) sm.flag[0] = sm.flag[1] = -1;
   __syncthreads();
+  // waves 0 .. NQ-1 score (32 query rows each), waves NQ and NQ+1 value
   if (wave == 0)
-    ring::score_wave<0>(sm, w, lane);
-  else if (wave == 1)
-    ring::score_wave<1>(sm, w, lane);
-  else if (wave == 2)
-    ring::value_wave<0>(sm, w, lane);
+    ring::score_wave<NQ, 0>(sm, w, lane);
+  else if (NQ == 2 && wave == 1)
+    ring::score_wave<NQ, (NQ == 2 ? 1 : 0)>(sm, w, lane);
+  else if (wave == NQ)
+    ring::value_wave<NQ, 0>(sm, w, lane);
   else
-    ring::value_wave<1>(sm, w, lane);
+    ring::value_wave<NQ, 1>(sm, w, lane);
 }
 
 }  // namespace
@@ -933,12 +566,12 @@ hipError_t launch_decode_absorbed_mfma(const mla_shape_t& s, const void* q_abs,
     if (v >= 0.f && v <= 64.f) slack = v;
   }
   if (nq == 2)
-    hipLaunchKernelGGL(decode_absorbed_mfma_ring_kernel, dim3(grid), dim3(256), 0, st,
+    hipLaunchKernelGGL(decode_absorbed_mfma_ring_kernel<2>, dim3(grid), dim3(256), 0, st,
                        static_cast<const bf16_t*>(q_abs), static_cast<const bf16_t*>(pool), pt,
                        lens, o_part, lse_part, s.s_q, s.n_heads, s.max_pages, s.n_splits,
                        s.split_tokens, zscale, slack, n_units, n_yblk);
   else
-    hipLaunchKernelGGL(decode_absorbed_mfma_rows32_kernel<1>, dim3(grid), dim3(128), 0, st,
+    hipLaunchKernelGGL(decode_absorbed_mfma_ring_kernel<1>, dim3(grid), dim3(192), 0, st,
                        static_cast<const bf16_t*>(q_abs), static_cast<const bf16_t*>(pool), pt,
                        lens, o_part, lse_part, s.s_q, s.n_heads, s.max_pages, s.n_splits,
                        s.split_tokens, zscale, slack, n_units, n_yblk);
