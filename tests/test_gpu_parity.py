@@ -119,6 +119,21 @@ def test_bf16_mtp_small_all_steps(ctx):
     check_absorbed_all_steps(make_inputs(cfg, seed=3), S=3)
 
 
+@pytest.mark.parametrize("S,ctx", [(9, [4096, 4096]), (3, [4096, 1, 64])])
+def test_chunks_past_the_last_page(S, ctx):
+    """Page tables exactly as long as the longest sequence, with trailing empty chunks
+    (their first token index points one page past the table row)."""
+    cfg = small(batch=len(ctx), ctx=("list", ctx))
+    check_absorbed_all_steps(make_inputs(cfg, seed=13, max_pages=max(ctx) // 64), S=S)
+
+
+@pytest.mark.parametrize("s_q,S,L", [(1, 5, 0), (2, 3, 0), (1, 11, 192)])
+def test_bf16_gqla_absorbed_shapes(s_q, S, L):
+    """32 query heads in 8 groups: 32-row workgroups at s_q = 1, 64-row ones at s_q = 2."""
+    cfg = get_config("gqla-b32-t8192", batch=3, s_q=s_q, ctx=("list", [700, 64, 1999]))
+    check_absorbed_all_steps(make_inputs(cfg, seed=14), S=S, split_tokens=L)
+
+
 def test_bf16_gqla_absorbed_small():
     cfg = get_config("gqla-b32-t8192", batch=3, ctx=("list", [500, 64, 1999]))
     check_absorbed_all_steps(make_inputs(cfg, seed=4), S=2)
@@ -291,6 +306,10 @@ def test_full_dsv2_b16_t4096():
 
 def test_full_long_b4_t131072():
     sampled_full_check(get_config("long-b4-t131072"), [0, 1, 2, 3], [0, 127, 45, 90])
+
+
+def test_full_gqla_b32_t65536_absorbed():
+    sampled_full_check(get_config("gqla-b32-t65536"), [0, 17, 31], list(range(32)))
 
 
 def test_full_mtp_b64_ragged():
