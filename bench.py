@@ -7,10 +7,13 @@ ABI of libmla.so on one HIP stream.  The workload (default: batch 4 x 131072-tok
 contexts, 128 heads, latent 512 + RoPE 64, bf16, split-KV over 32 chunks) is seeded and
 synthetic and is resident in HBM before timing starts.
 
-Every step is bracketed by HIP events recorded on the launch stream, with events between
-its four kernels; a 1 GiB fill between steps (outside the events) evicts the 256 MB
-last-level cache so every step reads the cache from HBM.  ms_per_step is the median
-step time (p10/p90 beside it).
+K timed steps run the whole step through one library call (`mla_decode_step`, four
+kernels) with HIP events on the launch stream around it only: ms_per_step is their median
+step time (p10/p90 beside it).  Interleaved with them run K instrumented steps through
+the four separate entry points with an event between kernels; they give the per-kernel
+times (`kernel_ms`) and the decode kernel's launch time that `roofline` uses.  A 1 GiB
+fill before every step (outside the events) evicts the 256 MB last-level cache so every
+step reads the cache from HBM.
 
 Prints ONE JSON line.  `value` is cached-latent-tokens/s of the whole step.
 `roofline` describes the decode kernel (the dominant one): algorithmic bytes (every
@@ -143,36 +146,47 @@ def time_workload(name, steps, warmup, splits=None, flush=True):
     sp = stream.cuda_stream
     fl = _flusher() if flush else (lambda: None)
 
-    def step(ev=None):
-        rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
-        rec(0)
+    def whole_step():
+        mla.mla_decode_step(sh, d.q, d.w_uk, d.w_uv, d.pool, d.page_table, d.ctx_lens,
+                            d.q_abs, op, d.lse_part, d.o_lat, d.out, d.lse, stream=sp)
+
+    def split_step(ev):
+        ev[0].record(stream)
         mla.mla_absorb_q(sh, d.q, d.w_uk, d.q_abs, stream=sp)
-        rec(1)
+        ev[1].record(stream)
         mla.mla_decode_absorbed(sh, d.q_abs, d.pool, d.page_table, d.ctx_lens, op,
                                 d.lse_part, stream=sp)
-        rec(2)
+        ev[2].record(stream)
         mla.mla_splitkv_combine(sh, cfg.d_c, op, d.lse_part, d.o_lat, d.lse, stream=sp)
-        rec(3)
+        ev[3].record(stream)
         mla.mla_out_uv(sh, d.o_lat, d.w_uv, d.out, stream=sp)
-        rec(4)
+        ev[4].record(stream)
 
     for _ in range(warmup):
         fl()
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        whole_step()
+    # The whole step (one library call, four kernels) with events only around it, and,
+    # interleaved with it so both see the same clocks, the same step through the four
+    # entry points with an event between kernels.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    evk = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         fl()
-        step(evs[i])
+        evs[i][0].record(stream)
+        whole_step()
+        evs[i][1].record(stream)
+        fl()
+        split_step(evk[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = {"step": [e[0].elapsed_time(e[4]) for e in evs],
-          "absorb_q": [e[0].elapsed_time(e[1]) for e in evs],
-          "decode": [e[1].elapsed_time(e[2]) for e in evs],
-          "combine": [e[2].elapsed_time(e[3]) for e in evs],
-          "out_uv": [e[3].elapsed_time(e[4]) for e in evs]}
+    ms = {"step": [e[0].elapsed_time(e[1]) for e in evs]}
+    ms.update({"step_with_kernel_events": [e[0].elapsed_time(e[4]) for e in evk],
+               "absorb_q": [e[0].elapsed_time(e[1]) for e in evk],
+               "decode": [e[1].elapsed_time(e[2]) for e in evk],
+               "combine": [e[2].elapsed_time(e[3]) for e in evk],
+               "out_uv": [e[3].elapsed_time(e[4]) for e in evk]})
     return inp, d, ms, wall / steps * 1e3
 
 
@@ -200,28 +214,36 @@ def time_gqa_path(name, steps, warmup, flush=True):
     op = d.o_part_view(cfg.d_v)
     fl = _flusher() if flush else (lambda: None)
 
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
+    def split_step(ev):
+        ev[0].record(stream)
         mla.gqla_decode_gqa(sh, d.q, k, v, kr, d.page_table, d.ctx_lens, op, d.lse_part,
                             stream=sp)
-        if ev:
-            ev[1].record(stream)
+        ev[1].record(stream)
         mla.mla_splitkv_combine(sh, cfg.d_v, op, d.lse_part, d.out, d.lse, stream=sp)
-        if ev:
-            ev[2].record(stream)
+        ev[2].record(stream)
+
+    def whole_step(ev):
+        ev[0].record(stream)
+        mla.gqla_decode_step(sh, d.q, k, v, kr, d.page_table, d.ctx_lens, op, d.lse_part,
+                             d.out, d.lse, stream=sp)
+        ev[1].record(stream)
 
     for _ in range(warmup):
         fl()
-        step()
+        whole_step([torch.cuda.Event(), torch.cuda.Event()])
+    # The whole step with events only around it, interleaved with the same step with an
+    # event between its kernels (the decode kernel's time for the roofline).
+    whole = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
         fl()
-        step(evs[i])
+        whole_step(whole[i])
+        fl()
+        split_step(evs[i])
     torch.cuda.synchronize()
     dec = _stats([e[0].elapsed_time(e[1]) for e in evs])[0]
-    core, p10, p90 = _stats([e[0].elapsed_time(e[2]) for e in evs])
+    core, p10, p90 = _stats([e[0].elapsed_time(e[1]) for e in whole])
     bpt = mla.gqla_cache_scalars_per_token(sh) * 2
     return {"workload": name, "path": "gqa", "decode_ms": dec, "core_ms": core,
             "core_ms_p10_p90": [p10, p90],
@@ -289,8 +311,9 @@ def main():
                    == 1 else "generic", "llc_flush_between_steps": not args.no_flush},
         "step_ms_p10_p90": [p10, p90],
         "kernel_ms": {k: _stats(v)[0] for k, v in ms.items() if k != "step"},
+        # decode + combine from the pass with events between kernels
         "core_ms": _stats([a + b for a, b in zip(ms["decode"], ms["combine"])])[0],
-        "wall_ms_per_step_incl_flush": wall_ms,
+        "wall_ms_per_step_incl_flushes_and_kernel_pass": wall_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "mla_decode_absorbed", "kernel_ms": dec_ms,

@@ -20,6 +20,12 @@ hipError_t launch_decode_absorbed_mfma(const mla_shape_t& s, const void* q_abs,
 bool decode_absorbed_mfma_supported(const mla_shape_t& s);
 hipError_t launch_combine(const mla_shape_t& s, int width, const float* o_part,
                           const float* lse_part, float* o, float* lse, hipStream_t st);
+// a3 + a4 in one launch for the absorbed step (bf16, d_c 512, d_v 128, <= 64 splits);
+// bitwise the same results as launch_combine followed by launch_out_uv
+bool combine_out_uv_supported(const mla_shape_t& s);
+hipError_t launch_combine_out_uv(const mla_shape_t& s, const float* o_part,
+                                 const float* lse_part, const void* w_uv, float* o_lat,
+                                 float* lse, float* out, hipStream_t st);
 hipError_t launch_out_uv(const mla_shape_t& s, const float* o_lat, const void* w_uv,
                          float* out, hipStream_t st);
 hipError_t launch_gqa_decode_generic(const mla_shape_t& s, const void* q, const void* k,

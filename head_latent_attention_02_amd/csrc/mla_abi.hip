@@ -159,6 +159,9 @@ mla_status_t mla_decode_step(const mla_shape_t* s, const void* q, const void* w_
   if (v != MLA_OK) return v;
   v = mla_decode_absorbed(s, q_abs, kv_pool, page_table, ctx_lens, o_part, lse_part, stream);
   if (v != MLA_OK) return v;
+  if (mla::combine_out_uv_supported(*s))
+    return hip_status(
+        mla::launch_combine_out_uv(*s, o_part, lse_part, w_uv, o_lat, lse, out, stream));
   v = mla_splitkv_combine(s, s->d_c, o_part, lse_part, o_lat, lse, stream);
   if (v != MLA_OK) return v;
   return mla_out_uv(s, o_lat, w_uv, out, stream);

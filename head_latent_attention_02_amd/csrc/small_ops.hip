@@ -10,13 +10,15 @@
 //     on GQLA, "The paper's summary").
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mla {
 namespace {
 
-constexpr int kQB = 8;  // queries per block in a1 / a4
+constexpr int kQB = 8;  // queries per block in a4, and in a1 above 4 queries
 
 // 8 consecutive elements: a raw chunk (one 16-byte load for bf16, two for fp32) and its
 // conversion to floats.  Kernels issue a batch of raw loads first and convert afterwards,
@@ -51,66 +53,74 @@ __device__ __forceinline__ void to_f32(const Raw8<float>& r, float (&x)[8]) {
 }
 
 // ---------------------------------------------------------------- a1 absorb
-// Block (head h, 256 latent columns, 8 queries), 256 threads.  Thread (rs, cl) = (tid / 32,
-// tid % 32) owns columns c0 + 8 cl .. +8 and weight rows rs, rs + 8, ...: each W_UK row
-// chunk is one 512-byte coalesced read per 32 lanes, and every weight byte of the block
-// is read once.
+// Block (head h, 256 latent columns, QB = 4 or 8 queries), 256 threads.  Thread
+// (rs, cl) = (tid / 32, tid % 32) owns columns c0 + 8 cl .. +8 and weight rows rs, rs + 8,
+// ...: each W_UK row chunk is one 512-byte coalesced read per 32 lanes, and every weight
+// byte of the block is read once.
 constexpr int kAbsCols = 256;
 constexpr int kAbsBatch = 16;   // weight rows per thread in flight at once
-template <typename T>
+template <typename T, int QB>
 __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
                                                        const T* __restrict__ w_uk,
                                                        T* __restrict__ q_abs, int NQ, int H,
                                                        int Hw, int d_n, int d_r, int d_c) {
   extern __shared__ float smem[];
-  float* qs = smem;                       // [d_n][kQB]: row i's 8 queries are 32 bytes
-  float* red = smem + kQB * d_n;          // [4 waves][kQB][kAbsCols]
-  const int h = blockIdx.x, c0 = blockIdx.y * kAbsCols, q0 = blockIdx.z * kQB;
+  float* qs = smem;                       // [d_n][QB]: row i's QB queries together
+  float* red = smem + QB * d_n;           // [4 waves][QB][kAbsCols]
+  const int h = blockIdx.x, c0 = blockIdx.y * kAbsCols, q0 = blockIdx.z * QB;
   const int w = h / (H / Hw);
-  const int nq = min(kQB, NQ - q0);
+  const int nq = min(QB, NQ - q0);
   const int dq = d_n + d_r, D = d_c + d_r;
   const int tid = threadIdx.x, rs = tid >> 5, cl = tid & 31;
+  const int c = c0 + 8 * cl;
+  const T* W = w_uk + static_cast<size_t>(w) * d_n * d_c + c;
+  // weight rows rs, rs + 8, ... in batches of kAbsBatch: a batch's loads are all issued
+  // before any is used, and the first batch (at d_n = 128 a thread's whole share) before
+  // the queries are staged, so the two reads overlap
+  Raw8<T> raw[kAbsBatch];
+  auto issue = [&](int i0) {
+#pragma unroll
+    for (int bt = 0; bt < kAbsBatch; ++bt) {
+      const int i = i0 + 8 * bt;
+      if (c < d_c && i < d_n) raw[bt] = load_raw8(W + static_cast<size_t>(i) * d_c);
+    }
+  };
+  issue(rs);
   // the queries' no-position parts, 8 elements per thread and load (one load each while
-  // kQB * d_n <= 8 * 256), transposed into qs
-  for (int idx = tid; idx < kQB * d_n / 8; idx += blockDim.x) {
+  // QB * d_n <= 8 * 256), transposed into qs
+  for (int idx = tid; idx < QB * d_n / 8; idx += blockDim.x) {
     const int per = d_n / 8;
     const int jq = idx / per, i8 = 8 * (idx - jq * per);
     float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (jq < nq) to_f32(load_raw8(q + (static_cast<size_t>(q0 + jq) * H + h) * dq + i8), x);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qs[(i8 + e) * kQB + jq] = x[e];
+    for (int e = 0; e < 8; ++e) qs[(i8 + e) * QB + jq] = x[e];
   }
   __syncthreads();
-  const int c = c0 + 8 * cl;
-  float acc[kQB][8];
+  float acc[QB][8];
 #pragma unroll
-  for (int jq = 0; jq < kQB; ++jq)
+  for (int jq = 0; jq < QB; ++jq)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[jq][e] = 0.f;
   if (c < d_c) {
-    const T* W = w_uk + static_cast<size_t>(w) * d_n * d_c + c;
-    // rows rs, rs + 8, ... in batches of kAbsBatch: the batch's loads are all issued before
-    // any is used (at d_n = 128 a thread's whole share is one batch)
     for (int i0 = rs; i0 < d_n; i0 += 8 * kAbsBatch) {
-      Raw8<T> raw[kAbsBatch];
-#pragma unroll
-      for (int bt = 0; bt < kAbsBatch; ++bt) {
-        const int i = i0 + 8 * bt;
-        if (i < d_n) raw[bt] = load_raw8(W + static_cast<size_t>(i) * d_c);
-      }
+      if (i0 != rs) issue(i0);
 #pragma unroll
       for (int bt = 0; bt < kAbsBatch; ++bt) {
         const int i = i0 + 8 * bt;
         if (i >= d_n) break;
         float wv[8];
         to_f32(raw[bt], wv);
-        // the row's 8 query values: two 16-byte LDS reads, the same address across a
+        // the row's QB query values: 16-byte LDS reads, the same address across a
         // half-wave (a broadcast)
-        const float4 qa = *reinterpret_cast<const float4*>(&qs[i * kQB]);
-        const float4 qb = *reinterpret_cast<const float4*>(&qs[i * kQB + 4]);
-        const float qv[kQB] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        float qv[QB];
 #pragma unroll
-        for (int jq = 0; jq < kQB; ++jq)
+        for (int k4 = 0; k4 < QB; k4 += 4) {
+          const float4 t = *reinterpret_cast<const float4*>(&qs[i * QB + k4]);
+          qv[k4] = t.x; qv[k4 + 1] = t.y; qv[k4 + 2] = t.z; qv[k4 + 3] = t.w;
+        }
+#pragma unroll
+        for (int jq = 0; jq < QB; ++jq)
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[jq][e] = fmaf(qv[jq], wv[e], acc[jq][e]);
       }
@@ -118,24 +128,24 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
   }
   // the two row slices of a wave (lane halves) meet by a shuffle, the 4 waves in LDS
 #pragma unroll
-  for (int jq = 0; jq < kQB; ++jq)
+  for (int jq = 0; jq < QB; ++jq)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[jq][e] += __shfl_xor(acc[jq][e], 32, 64);
   if ((rs & 1) == 0) {
 #pragma unroll
-    for (int jq = 0; jq < kQB; ++jq)
+    for (int jq = 0; jq < QB; ++jq)
 #pragma unroll
       for (int e = 0; e < 8; e += 4)
-        *reinterpret_cast<float4*>(&red[((rs >> 1) * kQB + jq) * kAbsCols + 8 * cl + e]) =
+        *reinterpret_cast<float4*>(&red[((rs >> 1) * QB + jq) * kAbsCols + 8 * cl + e]) =
             make_float4(acc[jq][e], acc[jq][e + 1], acc[jq][e + 2], acc[jq][e + 3]);
   }
   __syncthreads();
-  for (int idx = tid; idx < kQB * kAbsCols; idx += blockDim.x) {
+  for (int idx = tid; idx < QB * kAbsCols; idx += blockDim.x) {
     const int jq = idx / kAbsCols, cc = idx - jq * kAbsCols;
     if (jq >= nq || c0 + cc >= d_c) continue;
     float v = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v += red[(r * kQB + jq) * kAbsCols + cc];
+    for (int r = 0; r < 4; ++r) v += red[(r * QB + jq) * kAbsCols + cc];
     stf(q_abs + (static_cast<size_t>(q0 + jq) * H + h) * D + c0 + cc, v);
   }
   if (blockIdx.y == 0) {
@@ -149,6 +159,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
 
 // ---------------------------------------------------------------- a3 combine
 constexpr int kCombBatch = 32;
+constexpr int kCombWts = 2048;
 // Block per query row, 128 threads, 4 consecutive columns per thread per pass.
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
@@ -157,8 +168,20 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
                                                       int width) {
   const size_t row = blockIdx.x;
   const float* lp = lse_part + row * S;
+  const float* op = o_part + row * S * width;
   __shared__ float red[2][4];
+  __shared__ float wts[kCombWts];  // chunk weights e^{lse_u - max} of the first kCombWts
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;   // 128 threads = 2 waves
+  // the first batch of partials (at width 512 and S <= 32 a thread's whole share) is
+  // loaded while the chunk weights are reduced
+  float4 v[kCombBatch];
+  auto issue = [&](int c, int u0) {
+#pragma unroll
+    for (int b = 0; b < kCombBatch; ++b)
+      if (u0 + b < S)
+        v[b] = *reinterpret_cast<const float4*>(op + static_cast<size_t>(u0 + b) * width + c);
+  };
+  if (4 * threadIdx.x < width) issue(4 * threadIdx.x, 0);
   // row maximum and sum of the chunk weights, every thread taking splits t, t + 128, ...
   float m = -INFINITY;
   for (int u = threadIdx.x; u < S; u += blockDim.x) m = fmaxf(m, lp[u]);
@@ -174,28 +197,28 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   }
   const float ml = m * kLog2e;
   float tot = 0.f;
-  for (int u = threadIdx.x; u < S; u += blockDim.x) tot += exp2f(fmaf(lp[u], kLog2e, -ml));
+  for (int u = threadIdx.x; u < S; u += blockDim.x) {
+    const float e = exp2f(fmaf(lp[u], kLog2e, -ml));
+    if (u < kCombWts) wts[u] = e;
+    tot += e;
+  }
   tot = wave_sum(tot);
   if (lane == 0) red[1][wv] = tot;
   __syncthreads();
   tot = red[1][0] + red[1][1];
   const float inv = 1.f / tot;
-  const float* op = o_part + row * S * width;
   for (int c = 4 * threadIdx.x; c < width; c += 4 * blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     // splits in batches of kCombBatch whose loads are all issued before any is used; an
     // empty split (lse -inf, weight 0) may hold anything, so its values are selected
     // away, not scaled
     for (int u0 = 0; u0 < S; u0 += kCombBatch) {
-      float4 v[kCombBatch];
-#pragma unroll
-      for (int b = 0; b < kCombBatch; ++b)
-        if (u0 + b < S)
-          v[b] = *reinterpret_cast<const float4*>(op + static_cast<size_t>(u0 + b) * width + c);
+      if (u0 != 0 || c != 4 * static_cast<int>(threadIdx.x)) issue(c, u0);
 #pragma unroll
       for (int b = 0; b < kCombBatch; ++b) {
         if (u0 + b >= S) break;
-        const float wgt = exp2f(fmaf(lp[u0 + b], kLog2e, -ml));
+        const float wgt = u0 + b < kCombWts ? wts[u0 + b]
+                                            : exp2f(fmaf(lp[u0 + b], kLog2e, -ml));
         const bool use = wgt > 0.f;
         acc.x = fmaf(wgt, use ? v[b].x : 0.f, acc.x);
         acc.y = fmaf(wgt, use ? v[b].y : 0.f, acc.y);
@@ -294,39 +317,43 @@ __global__ __launch_bounds__(256) void out_uv_kernel(const float* __restrict__ o
 // a4 on the matrix cores (bf16 weights): out^T[v][n] = sum_c W_UV[w(h)][v][c] o[n][h][c] as
 // v_mfma_f32_32x32x16_bf16 with the weight rows as the A operand (v = M, c = K, both in
 // their natural row-major layout) and the latent outputs, rounded to bf16, as the B
-// operand (query = N, padded to 32).  One wave per (head, 32 value rows); query blocks
-// of 32 in turn.  Loads run kUvmSteps K-steps ahead of their MFMAs.
+// operand (query = N, padded to 32).  One block of 4 waves per (head, 32 value rows); the
+// waves split the latent dimension (at d_c = 512 each issues all its loads at once) and
+// meet in LDS; query blocks of 32 in turn.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kUvmSteps = 8;
+constexpr int kUvmWaves = 4;
 
-__global__ __launch_bounds__(64) void out_uv_mfma_kernel(const float* __restrict__ o_lat,
-                                                         const bf16_t* __restrict__ w_uv,
-                                                         float* __restrict__ out, int NQ,
-                                                         int H, int Hw, int d_c, int d_v) {
+__global__ __launch_bounds__(64 * kUvmWaves) void out_uv_mfma_kernel(
+    const float* __restrict__ o_lat, const bf16_t* __restrict__ w_uv, float* __restrict__ out,
+    int NQ, int H, int Hw, int d_c, int d_v) {
+  __shared__ float red[kUvmWaves - 1][16][64];
   const int h = blockIdx.x, v0 = 32 * blockIdx.y;
   const int w = h / (H / Hw);
-  const int lane = threadIdx.x, m = lane & 31, g = lane >> 5;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m = lane & 31, g = lane >> 5;
   const int n_k = d_c / 16;
+  const int per = (n_k + kUvmWaves - 1) / kUvmWaves;
+  const int kb = wave * per, ke = min(n_k, kb + per);   // this wave's K-steps
   const int v = min(v0 + m, d_v - 1);   // rows past d_v read a valid row, never stored
   const bf16_t* wr = w_uv + (static_cast<size_t>(w) * d_v + v) * d_c + 8 * g;
   for (int n0 = 0; n0 < NQ; n0 += 32) {
     const int n = n0 + m;
     const float* orow = o_lat + (static_cast<size_t>(min(n, NQ - 1)) * H + h) * d_c + 8 * g;
     f32x16_t acc = {};
-    for (int k0 = 0; k0 < n_k; k0 += kUvmSteps) {
+    for (int k0 = kb; k0 < ke; k0 += kUvmSteps) {
       uint4 a[kUvmSteps];
       float4 b[kUvmSteps][2];
 #pragma unroll
       for (int t = 0; t < kUvmSteps; ++t) {
-        const int ks = min(k0 + t, n_k - 1);
+        const int ks = min(k0 + t, ke - 1);
         a[t] = *reinterpret_cast<const uint4*>(wr + 16 * ks);
         b[t][0] = *reinterpret_cast<const float4*>(orow + 16 * ks);
         b[t][1] = *reinterpret_cast<const float4*>(orow + 16 * ks + 4);
       }
 #pragma unroll
       for (int t = 0; t < kUvmSteps; ++t) {
-        if (k0 + t >= n_k) break;
+        if (k0 + t >= ke) break;
         bf16x8_t bv;
         bv[0] = static_cast<__bf16>(b[t][0].x); bv[1] = static_cast<__bf16>(b[t][0].y);
         bv[2] = static_cast<__bf16>(b[t][0].z); bv[3] = static_cast<__bf16>(b[t][0].w);
@@ -337,14 +364,157 @@ __global__ __launch_bounds__(64) void out_uv_mfma_kernel(const float* __restrict
                                                       acc, 0, 0, 0);
       }
     }
+    if (wave > 0) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) red[wave - 1][j][lane] = acc[j];
+    }
+    __syncthreads();
     // lane (query n, half g) holds value rows 8 (j / 4) + 4 g + j % 4 of the block
-    if (n < NQ) {
+    if (wave == 0 && n < NQ) {
       float* orow_out = out + (static_cast<size_t>(n) * H + h) * d_v + v0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
+        float t = acc[j];
+#pragma unroll
+        for (int r = 0; r < kUvmWaves - 1; ++r) t += red[r][j][lane];
         const int vv = 8 * (j >> 2) + 4 * g + (j & 3);
-        if (v0 + vv < d_v) orow_out[vv] = acc[j];
+        if (v0 + vv < d_v) orow_out[vv] = t;
       }
+    }
+    __syncthreads();   // red is reused by the next query block
+  }
+}
+
+// ---------------------------------------------------------------- a3 + a4 fused
+// The step's split merge and value up-projection in one launch (bf16 weights, d_c = 512,
+// d_v = 128, at most 64 splits).  Block (head h, 32 queries), 8 waves.  Arithmetic is the
+// same, operation for operation, as combine_kernel followed by out_uv_mfma_kernel, so the
+// results are bitwise those of the two separate entry points; what changes is that the
+// merged latent rows go to the up-projection through LDS and that the weight loads, the
+// partial loads and the lse reductions are all in flight together.
+//   wave w: value rows 32 (w % 4) .. +32 and latent quarters 2 (w / 4), 2 (w / 4) + 1 of
+//   the up-projection; all waves share the merge (4 queries x 512 columns per pass).
+constexpr int kFuQ = 32;          // queries per block
+constexpr int kFuBatch = 16;      // partial loads per thread in flight at once
+constexpr int kFuRow = 512 + 8;   // bf16 elements per LDS row of merged latents (padded)
+
+__global__ __launch_bounds__(512) void combine_out_uv_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part,
+    const bf16_t* __restrict__ w_uv, float* __restrict__ o_lat, float* __restrict__ lse,
+    float* __restrict__ out, int NQ, int H, int Hw, int S) {
+  constexpr int d_c = 512, d_v = 128;
+  __shared__ __align__(16) bf16_t ob[kFuQ * kFuRow];   // merged latents as MFMA B rows
+  __shared__ float wts[kFuQ][64];                       // chunk weights e^{lse_u - max}
+  __shared__ float inv_s[kFuQ];
+  __shared__ float red[4][2][16][64];                   // quarters 2, 3 per value block
+  const int h = blockIdx.x, q0 = blockIdx.y * kFuQ;
+  const int nqb = min(kFuQ, NQ - q0);
+  const int w = h / (H / Hw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 31, g = lane >> 5, vb = wave & 3, kh = wave >> 2;
+
+  // (1) this wave's weight rows: 16 K-steps of 16 latent columns, all in flight
+  uint4 a[16];
+  {
+    const bf16_t* wr = w_uv + (static_cast<size_t>(w) * d_v + 32 * vb + m) * d_c + 8 * g;
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      a[t] = *reinterpret_cast<const uint4*>(wr + 16 * (16 * kh + t));
+  }
+  // (2) the first batch of partials of merge pass 0
+  const int cq = tid >> 7, c4 = 4 * (tid & 127);
+  float4 v[kFuBatch];
+  auto issue = [&](int n, int u0) {
+    const float* op = o_part + (static_cast<size_t>(q0 + n) * H + h) * S * d_c + c4;
+#pragma unroll
+    for (int b = 0; b < kFuBatch; ++b)
+      if (u0 + b < S) v[b] = *reinterpret_cast<const float4*>(op + static_cast<size_t>(u0 + b) * d_c);
+  };
+  if (cq < nqb) issue(cq, 0);
+  // (3) chunk weights, 1 / sum and lse of every query: one wave per query, lane = split
+  for (int n = wave; n < kFuQ; n += 8) {
+    float l = -INFINITY;
+    if (n < nqb && lane < S) l = lse_part[(static_cast<size_t>(q0 + n) * H + h) * S + lane];
+    float mx = l;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    float e = 0.f, inv = 0.f;
+    if (mx != -INFINITY) {
+      const float ml = mx * kLog2e;
+      float tot = 0.f;
+      if (lane < S) {
+        e = exp2f(fmaf(l, kLog2e, -ml));
+        tot += e;
+      }
+      tot = wave_sum(tot);
+      inv = 1.f / tot;
+      if (lane == 0 && lse) lse[static_cast<size_t>(q0 + n) * H + h] = mx + logf(tot);
+    } else if (lane == 0 && lse && n < nqb) {
+      lse[static_cast<size_t>(q0 + n) * H + h] = -INFINITY;
+    }
+    wts[n][lane] = e;
+    if (lane == 0) inv_s[n] = inv;
+  }
+  __syncthreads();
+  // (4) merge, 4 queries x 512 columns per pass; rows past the block's queries are zeros
+  for (int n = cq; n < kFuQ; n += 4) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (n < nqb) {
+      for (int u0 = 0; u0 < S; u0 += kFuBatch) {
+        if (n != cq || u0 != 0) issue(n, u0);
+#pragma unroll
+        for (int b = 0; b < kFuBatch; ++b) {
+          if (u0 + b >= S) break;
+          const float wgt = wts[n][u0 + b];
+          const bool use = wgt > 0.f;
+          acc.x = fmaf(wgt, use ? v[b].x : 0.f, acc.x);
+          acc.y = fmaf(wgt, use ? v[b].y : 0.f, acc.y);
+          acc.z = fmaf(wgt, use ? v[b].z : 0.f, acc.z);
+          acc.w = fmaf(wgt, use ? v[b].w : 0.f, acc.w);
+        }
+      }
+      const float inv = inv_s[n];
+      acc = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+      *reinterpret_cast<float4*>(o_lat + (static_cast<size_t>(q0 + n) * H + h) * d_c + c4) = acc;
+    }
+    const uint32_t bx = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc.x));
+    const uint32_t by = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc.y));
+    const uint32_t bz = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc.z));
+    const uint32_t bw = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc.w));
+    *reinterpret_cast<uint2*>(ob + n * kFuRow + c4) = make_uint2(bx | (by << 16), bz | (bw << 16));
+  }
+  __syncthreads();
+  // (5) up-projection: two latent quarters per wave, each accumulated from zero
+  f32x16_t acc2[2] = {{}, {}};
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int ks = 16 * kh + 8 * qq + t;
+      const bf16x8_t bv =
+          *reinterpret_cast<const bf16x8_t*>(ob + m * kFuRow + 16 * ks + 8 * g);
+      acc2[qq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8_t, a[8 * qq + t]), bv, acc2[qq], 0, 0, 0);
+    }
+  if (kh == 1) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      red[vb][0][j][lane] = acc2[0][j];
+      red[vb][1][j][lane] = acc2[1][j];
+    }
+  }
+  __syncthreads();
+  // lane (query m, half g) holds value rows 8 (j / 4) + 4 g + j % 4 of block vb; the
+  // quarters are summed in order 0, 1, 2, 3
+  if (kh == 0 && m < nqb) {
+    float* orow = out + (static_cast<size_t>(q0 + m) * H + h) * d_v + 32 * vb;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float t = acc2[0][j];
+      t += acc2[1][j];
+      t += red[vb][0][j][lane];
+      t += red[vb][1][j][lane];
+      orow[8 * (j >> 2) + 4 * g + (j & 3)] = t;
     }
   }
 }
@@ -433,18 +603,26 @@ __global__ __launch_bounds__(256) void expand_kernel(const T* __restrict__ pool,
 hipError_t launch_absorb_q(const mla_shape_t& s, const void* q, const void* w_uk,
                            void* q_abs, hipStream_t st) {
   const int NQ = s.batch * s.s_q;
-  dim3 grid(s.n_heads, (s.d_c + kAbsCols - 1) / kAbsCols, (NQ + kQB - 1) / kQB);
-  const size_t lds = sizeof(float) * kQB * (s.d_nope + 4 * kAbsCols);
-  if (s.dtype == MLA_F32)
-    hipLaunchKernelGGL(absorb_q_kernel<float>, grid, dim3(256), lds, st,
-                       static_cast<const float*>(q), static_cast<const float*>(w_uk),
-                       static_cast<float*>(q_abs), NQ, s.n_heads, s.n_wheads, s.d_nope,
-                       s.d_rope, s.d_c);
+  // 4 queries per block when there are at most 4 (no idle accumulators), else 8
+  auto go = [&](auto qb) {
+    constexpr int QB = decltype(qb)::value;
+    dim3 grid(s.n_heads, (s.d_c + kAbsCols - 1) / kAbsCols, (NQ + QB - 1) / QB);
+    const size_t lds = sizeof(float) * QB * (s.d_nope + 4 * kAbsCols);
+    if (s.dtype == MLA_F32)
+      hipLaunchKernelGGL((absorb_q_kernel<float, QB>), grid, dim3(256), lds, st,
+                         static_cast<const float*>(q), static_cast<const float*>(w_uk),
+                         static_cast<float*>(q_abs), NQ, s.n_heads, s.n_wheads, s.d_nope,
+                         s.d_rope, s.d_c);
+    else
+      hipLaunchKernelGGL((absorb_q_kernel<bf16_t, QB>), grid, dim3(256), lds, st,
+                         static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(w_uk),
+                         static_cast<bf16_t*>(q_abs), NQ, s.n_heads, s.n_wheads, s.d_nope,
+                         s.d_rope, s.d_c);
+  };
+  if (NQ <= 4)
+    go(std::integral_constant<int, 4>{});
   else
-    hipLaunchKernelGGL(absorb_q_kernel<bf16_t>, grid, dim3(256), lds, st,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(w_uk),
-                       static_cast<bf16_t*>(q_abs), NQ, s.n_heads, s.n_wheads, s.d_nope,
-                       s.d_rope, s.d_c);
+    go(std::integral_constant<int, kQB>{});
   return hipGetLastError();
 }
 
@@ -466,13 +644,27 @@ hipError_t launch_out_uv(const mla_shape_t& s, const float* o_lat, const void* w
                        static_cast<const float*>(w_uv), out, NQ, s.n_heads, s.n_wheads,
                        s.d_c, s.d_v);
   else if (s.d_c % 16 == 0)
-    hipLaunchKernelGGL(out_uv_mfma_kernel, dim3(s.n_heads, (s.d_v + 31) / 32), dim3(64), 0,
-                       st, o_lat, static_cast<const bf16_t*>(w_uv), out, NQ, s.n_heads,
-                       s.n_wheads, s.d_c, s.d_v);
+    hipLaunchKernelGGL(out_uv_mfma_kernel, dim3(s.n_heads, (s.d_v + 31) / 32),
+                       dim3(64 * kUvmWaves), 0, st, o_lat, static_cast<const bf16_t*>(w_uv),
+                       out, NQ, s.n_heads, s.n_wheads, s.d_c, s.d_v);
   else
     hipLaunchKernelGGL(out_uv_kernel<bf16_t>, grid, dim3(256), lds, st, o_lat,
                        static_cast<const bf16_t*>(w_uv), out, NQ, s.n_heads, s.n_wheads,
                        s.d_c, s.d_v);
+  return hipGetLastError();
+}
+
+bool combine_out_uv_supported(const mla_shape_t& s) {
+  return s.dtype == MLA_BF16 && s.d_c == 512 && s.d_v == 128 && s.n_splits <= 64;
+}
+
+hipError_t launch_combine_out_uv(const mla_shape_t& s, const float* o_part,
+                                 const float* lse_part, const void* w_uv, float* o_lat,
+                                 float* lse, float* out, hipStream_t st) {
+  const int NQ = s.batch * s.s_q;
+  hipLaunchKernelGGL(combine_out_uv_kernel, dim3(s.n_heads, (NQ + kFuQ - 1) / kFuQ), dim3(512),
+                     0, st, o_part, lse_part, static_cast<const bf16_t*>(w_uv), o_lat, lse,
+                     out, NQ, s.n_heads, s.n_wheads, s.n_splits);
   return hipGetLastError();
 }
 

@@ -106,6 +106,39 @@ def test_tiny_f32_step_entry_point_matches_steps():
 
 # ------------------------------------------------------------- bf16, small sizes
 
+@pytest.mark.parametrize("name,s_q,ctx,S", [
+    ("dsv2-b16-t4096", 1, [4096, 577, 64, 33], 32),
+    ("dsv2-b16-t4096", 2, [1 + (97 * i) % 300 for i in range(20)], 3),
+    ("dsv2-b16-t4096", 1, [5000, 64], 64),
+    ("dsv2-b16-t4096", 2, [1, 2, 130], 1),
+    ("gqla-b32-t8192", 2, [700, 64, 1999], 5),
+])
+def test_bf16_step_entry_point_matches_steps(name, s_q, ctx, S):
+    """At bf16 with d_c 512 and d_v 128 the step entry point merges the splits and
+    up-projects in one kernel; its outputs must equal those of the separate entry points
+    bit for bit (20 sequences at s_q = 2 give two query blocks of 32, the second ragged;
+    s_q = 2 over one token gives rows with no visible token), and match the oracle."""
+    cfg = get_config(name, batch=len(ctx), s_q=s_q, ctx=("list", ctx))
+    inp = make_inputs(cfg, seed=21)
+    announce(f"case {name} s_q={s_q} ctx={ctx[:6]} S={S}")
+    d = DeviceInputs(inp, n_splits=S)
+    absorbed_step(d)
+    want = [t.clone() for t in (d.out, d.lse, d.o_lat)]
+    for t in (d.out, d.lse, d.o_lat):
+        t.fill_(7.0)
+    mla.mla_decode_step(d.shape, d.q, d.w_uk, d.w_uv, d.pool, d.page_table, d.ctx_lens,
+                        d.q_abs, d.o_part, d.lse_part, d.o_lat, d.out, d.lse)
+    torch.cuda.synchronize()
+    for got, exp, what in zip((d.out, d.lse, d.o_lat), want, ("out", "lse", "o_lat")):
+        assert torch.equal(got, exp), f"{what} differs from the separate entry points"
+    c = inp.cfg
+    out, lse = ref.mla_decode_naive(inp.q, inp.pool_view(), inp.page_table, inp.ctx_lens,
+                                    inp.w_uk, inp.w_uv, c.scale, c.page_size, c.d_c)
+    assert rel_err(d.out.cpu().numpy(), out) <= TOL["bf16"]
+    assert rel_err(d.lse.cpu().numpy(), lse) <= TOL["bf16"]
+
+
+
 @pytest.mark.parametrize("S,L,ctx", [
     (1, 0, [1000, 64]), (4, 0, [4096, 577]), (3, 128, [300, 129]), (8, 0, [33, 1])])
 def test_bf16_mla_small_all_steps(S, L, ctx):
