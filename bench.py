@@ -325,7 +325,8 @@ def main():
     print(json.dumps(line), flush=True)
     if args.extra:
         del d
-        for name in ("dsv2-b16-t4096", "mtp-b64-ragged", "gqla-b32-t65536"):
+        for name in ("dsv2-b16-t4096", "mtp-b64-ragged", "gqla-b32-t65536",
+                     "gqla-mtp-b32-t65536"):
             i2, d2, ms2, _ = time_workload(name, args.steps, args.warmup,
                                            flush=not args.no_flush)
             st2, dm2 = _stats(ms2["step"])[0], _stats(ms2["decode"])[0]
@@ -337,7 +338,8 @@ def main():
                               "decode_GBs": b2 / (dm2 * 1e-3) / 1e9}), file=sys.stderr,
                   flush=True)
             del d2
-        for name in ("gqla-b32-t8192", "gqla-b32-t65536"):
+        for name in ("gqla-b32-t8192", "gqla-b32-t65536", "gqla-mtp-b32-t65536",
+                     "gqla-shard-b32-t65536"):
             print(json.dumps(time_gqa_path(name, args.steps, args.warmup,
                                            flush=not args.no_flush)),
                   file=sys.stderr, flush=True)

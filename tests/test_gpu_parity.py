@@ -251,11 +251,19 @@ def expanded_pools(d):
 
 @pytest.mark.parametrize("dtype,ctx,S", [("f32", [300, 64, 1], 3), ("bf16", [1000, 129], 2),
                                          ("bf16", [4096, 2000], 4),
-                                         ("bf16", [1, 33, 64, 65, 95], 8)])
+                                         ("bf16", [1, 33, 64, 65, 95], 8),
+                                         ("shard", [1, 700, 2049], 5),
+                                         ("mtp", [1, 2, 130, 1999], 3)])
 def test_gqla_expand_and_gqa_path(dtype, ctx, S):
     if dtype == "f32":
         cfg = Config("gqla-tiny-f32", "f32", len(ctx), 1, 8, 2, 64, 16, 32, 32,
                      ("list", ctx), S)
+    elif dtype == "shard":   # one group and its 4 heads
+        cfg = get_config("gqla-shard-b32-t65536", batch=len(ctx), ctx=("list", ctx),
+                         n_splits=S)
+    elif dtype == "mtp":     # s_q = 2
+        cfg = get_config("gqla-mtp-b32-t65536", batch=len(ctx), ctx=("list", ctx),
+                         n_splits=S)
     else:
         cfg = get_config("gqla-b32-t8192", batch=len(ctx), ctx=("list", ctx), n_splits=S)
     inp = make_inputs(cfg, seed=9)
@@ -264,7 +272,7 @@ def test_gqla_expand_and_gqa_path(dtype, ctx, S):
     k, v, kr = expanded_pools(d)
     mla.gqla_expand_cache(d.shape, d.pool, d.w_uk, d.w_uv, k, v, kr)
     torch.cuda.synchronize()
-    tol = TOL[dtype]
+    tol = TOL[cfg.dtype]
     # a6 against the oracle's expansion (rows past the context are NaN on both sides)
     ek, ev, ekr = ref.expand_cache(inp.pool_f32(), inp.w_uk, inp.w_uv, cfg.d_c)
     fin = np.isfinite(ek)
@@ -349,9 +357,13 @@ def test_full_mtp_b64_ragged():
     sampled_full_check(get_config("mtp-b64-ragged"), [0, 17, 40, 63], [0, 127, 77])
 
 
-def test_full_gqla_b32_t65536_gqa_path():
-    """GQA path at its largest size: 32 sequences of 65536 tokens, expanded on the GPU."""
-    cfg = get_config("gqla-b32-t65536")
+@pytest.mark.parametrize("name", ["gqla-b32-t65536", "gqla-mtp-b32-t65536",
+                                  "gqla-shard-b32-t65536"])
+def test_full_gqla_b32_t65536_gqa_path(name):
+    """GQA path at its largest size: 32 sequences of 65536 tokens, expanded on the GPU; the
+    same at s_q = 2 (two query rows per head, causal), and one rank's share under 8-way
+    tensor parallelism over the groups (one group, 4 heads)."""
+    cfg = get_config(name)
     inp = make_inputs(cfg)
     announce(f"case full gqa {cfg.name} tokens={inp.total_tokens} S={cfg.n_splits}")
     d = DeviceInputs(inp)

@@ -63,6 +63,14 @@ CONFIGS = {
                               ("fixed", 32768), 8),
     "gqla-b32-t65536": Config("gqla-b32-t65536", "bf16", 32, 1, 32, 8, 512, 64, 128, 128,
                               ("fixed", 65536), 16),
+    # the same model decoding two tokens per step (MTP, s_q = 2), the pairing the pages
+    # give for the GQA path on H20
+    "gqla-mtp-b32-t65536": Config("gqla-mtp-b32-t65536", "bf16", 32, 2, 32, 8, 512, 64, 128,
+                                  128, ("fixed", 65536), 16),
+    # one rank's share of the GQA path under 8-way tensor parallelism over the groups:
+    # one group (its K, V and a replica of the RoPE key) and its 4 query heads
+    "gqla-shard-b32-t65536": Config("gqla-shard-b32-t65536", "bf16", 32, 1, 4, 1, 512, 64,
+                                    128, 128, ("fixed", 65536), 16),
 }
 
 
