@@ -14,11 +14,16 @@ Everything here is plain numpy in float64, written from the pages' definitions:
               up-projection) and of the GQLA per-group path and cache expansion.
 * ``brute`` - the same naive attention as pure-Python scalar loops, for tiny shapes,
               used to pin ``mla`` against an independent implementation.
+* ``append`` - the cache-append step on the write side: latent down-projection, RoPE
+              key projection and rotation, paged write of the new tokens' rows.
 
 Parity status: every function in ``mla`` is pinned by tests/test_oracle.py against
 something other than itself (pure-Python brute force, torch's scaled-dot-product
 attention as a library routine, closed forms for special cases, the absorbed/expanded
 and MQA-absorb/GQA-path equivalences the pages state, and the cache sizes the pages
-print).  No function here is "parity unpinned".
+print); every function in ``append`` by tests/test_oracle_append.py (the rotation's
+group properties, a complex-number formulation, pure-Python loops, closed forms and the
+positions the decode path's visibility rule fixes).  No function here is "parity
+unpinned".
 """
-from . import mla, brute  # noqa: F401
+from . import mla, brute, append  # noqa: F401
