@@ -253,6 +253,44 @@ def time_gqa_path(name, steps, warmup, flush=True):
             "kernel": "mfma" if mla.gqla_decode_kernel_kind(sh) == 1 else "generic"}
 
 
+def time_append(name, steps, warmup, d_model=5120, flush=True):
+    """Cache-append step (write side): the step's new tokens projected, rotated and
+    written into the paged cache."""
+    import torch
+    import head_latent_attention_02_amd as mla
+    from workloads import get_config, make_inputs, make_append_inputs
+    from workloads.device import DeviceInputs, to_dev
+
+    cfg = get_config(name)
+    inp = make_inputs(cfg)
+    ap = make_append_inputs(cfg, d_model=d_model)
+    d = DeviceInputs(inp)
+    h, w_dkv, w_kr = (to_dev(x, cfg.dtype) for x in (ap.h, ap.w_dkv, ap.w_kr))
+    stream = torch.cuda.current_stream()
+    fl = _flusher() if flush else (lambda: None)
+
+    def step():
+        mla.mla_cache_append(d.shape, d_model, 10000.0, h, w_dkv, w_kr, d.page_table,
+                             d.ctx_lens, d.pool, stream=stream.cuda_stream)
+
+    for _ in range(warmup):
+        fl()
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        fl()
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = _stats([e[0].elapsed_time(e[1]) for e in evs])[0]
+    wbytes = (cfg.d_c + cfg.d_rope) * d_model * (2 if cfg.dtype == "bf16" else 4)
+    return {"workload": name, "path": "append", "d_model": d_model,
+            "new_tokens": cfg.batch * cfg.s_q, "ms": ms,
+            "weight_GBs": wbytes / (ms * 1e-3) / 1e9}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -342,6 +380,10 @@ def main():
                      "gqla-shard-b32-t65536"):
             print(json.dumps(time_gqa_path(name, args.steps, args.warmup,
                                            flush=not args.no_flush)),
+                  file=sys.stderr, flush=True)
+        for name in ("long-b4-t131072", "mtp-b64-ragged"):
+            print(json.dumps(time_append(name, args.steps, args.warmup,
+                                         flush=not args.no_flush)),
                   file=sys.stderr, flush=True)
 
 

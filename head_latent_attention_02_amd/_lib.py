@@ -17,7 +17,8 @@ MLA_F32, MLA_BF16 = 0, 1
 
 # every symbol include/mla.h declares
 EXPORTS = ("mla_absorb_q", "mla_decode_absorbed", "mla_splitkv_combine", "mla_out_uv",
-           "gqla_decode_gqa", "gqla_expand_cache", "mla_decode_step", "gqla_decode_step",
+           "gqla_decode_gqa", "gqla_expand_cache", "mla_cache_append", "mla_decode_step",
+           "gqla_decode_step",
            "mla_cache_scalars_per_token", "gqla_cache_scalars_per_token",
            "mla_decode_kernel_kind", "gqla_decode_kernel_kind", "mla_status_str")
 
@@ -62,6 +63,7 @@ def load():
             "mla_out_uv": [S, P, P, P, P],
             "gqla_decode_gqa": [S, P, P, P, P, P, P, P, P, P],
             "gqla_expand_cache": [S, P, P, P, P, P, P, P],
+            "mla_cache_append": [S, ctypes.c_int32, ctypes.c_float, P, P, P, P, P, P, P],
             "mla_decode_step": [S, P, P, P, P, P, P, P, P, P, P, P, P, P],
             "gqla_decode_step": [S, P, P, P, P, P, P, P, P, P, P, P],
         }
@@ -149,6 +151,12 @@ def gqla_expand_cache(shape, kv_pool, w_uk, w_uv, k_pool, v_pool, kr_pool, strea
                       check=True):
     return _call("gqla_expand_cache", shape, (kv_pool, w_uk, w_uv, k_pool, v_pool, kr_pool),
                  stream, check)
+
+
+def mla_cache_append(shape, d_model, rope_base, h, w_dkv, w_kr, page_table, ctx_lens,
+                     kv_pool, stream=None, check=True):
+    return _call("mla_cache_append", shape, (h, w_dkv, w_kr, page_table, ctx_lens, kv_pool),
+                 stream, check, mid=(int(d_model), float(rope_base)))
 
 
 def mla_decode_step(shape, q, w_uk, w_uv, kv_pool, page_table, ctx_lens, q_abs, o_part,

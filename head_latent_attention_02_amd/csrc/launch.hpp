@@ -37,6 +37,10 @@ hipError_t launch_gqa_decode_mfma(const mla_shape_t& s, const void* q, const voi
                                   const int32_t* lens, float* o_part, float* lse_part,
                                   hipStream_t st);
 bool gqa_decode_mfma_supported(const mla_shape_t& s);
+hipError_t launch_cache_append(const mla_shape_t& s, int d_model, float rope_base,
+                               const void* h, const void* w_dkv, const void* w_kr,
+                               const int32_t* page_table, const int32_t* ctx_lens,
+                               void* pool, hipStream_t st);
 hipError_t launch_expand_cache(const mla_shape_t& s, const void* pool, const void* w_uk,
                                const void* w_uv, void* k, void* v, void* kr,
                                hipStream_t st);

@@ -145,6 +145,20 @@ mla_status_t gqla_expand_cache(const mla_shape_t* s, const void* kv_pool, const 
       mla::launch_expand_cache(*s, kv_pool, w_uk, w_uv, k_pool, v_pool, kr_pool, stream));
 }
 
+mla_status_t mla_cache_append(const mla_shape_t* s, int32_t d_model, float rope_base,
+                              const void* h, const void* w_dkv, const void* w_kr,
+                              const int32_t* page_table, const int32_t* ctx_lens,
+                              void* kv_pool, hipStream_t stream) {
+  mla_status_t v = validate(s);
+  if (v != MLA_OK) return v;
+  if (!h || !w_dkv || !w_kr || !page_table || !ctx_lens || !kv_pool) return MLA_ERR_NULL;
+  if (d_model <= 0 || !(rope_base > 0.f) || !isfinite(rope_base)) return MLA_ERR_SHAPE;
+  if (!mult8(d_model)) return MLA_ERR_UNSUPPORTED;
+  if ((static_cast<int64_t>(s->batch) * s->s_q + 7) / 8 > 65535) return MLA_ERR_UNSUPPORTED;
+  return hip_status(mla::launch_cache_append(*s, d_model, rope_base, h, w_dkv, w_kr,
+                                             page_table, ctx_lens, kv_pool, stream));
+}
+
 mla_status_t mla_decode_step(const mla_shape_t* s, const void* q, const void* w_uk,
                              const void* w_uv, const void* kv_pool, const int32_t* page_table,
                              const int32_t* ctx_lens, void* q_abs, float* o_part,

@@ -145,6 +145,23 @@ mla_status_t gqla_expand_cache(const mla_shape_t* shape, const void* kv_pool,
                                const void* w_uk, const void* w_uv, void* k_pool,
                                void* v_pool, void* kr_pool, hipStream_t stream);
 
+/* Cache append, the write side of a step: for every new token (b, s) at position
+ * t = ctx_lens[b] - s_q + s (the last token query row s sees):
+ *   c   = w_dkv @ h[b,s]                      (d_c)
+ *   k^R = RoPE_t(w_kr @ h[b,s])               (d_rope; pairs (2i, 2i+1) turned by
+ *                                              t * rope_base^(-2i / d_rope))
+ *   kv_pool[page_table[b][t / P], t % P, :] = [c ; k^R]   (fp32 accumulate, one rounding)
+ * h [B, s_q, d_model] dtype;  w_dkv [d_c, d_model] dtype;  w_kr [d_rope, d_model] dtype.
+ * d_model must be a multiple of 8 (else MLA_ERR_UNSUPPORTED) and rope_base > 0.  Tokens
+ * with t < 0, or whose page-table entry is negative or >= num_pages, are not written; no
+ * other pool row is touched.  Pages: "MLA and GRPO architecture" s.2, "The Mathematics of
+ * MLA" (c = W_DKV h) and "Decoupled Rotary Position Embeddings" (only the dedicated key is
+ * rotated); the rotation convention and the key's projection are not on the pages. */
+mla_status_t mla_cache_append(const mla_shape_t* shape, int32_t d_model, float rope_base,
+                              const void* h, const void* w_dkv, const void* w_kr,
+                              const int32_t* page_table, const int32_t* ctx_lens,
+                              void* kv_pool, hipStream_t stream);
+
 /* Whole absorbed step a1 -> a2 -> a3 -> a4 on one stream.  The caller provides the
  * workspaces: q_abs [B,s_q,H,D] dtype, o_part [B,s_q,H,S,d_c] fp32,
  * lse_part [B,s_q,H,S] fp32, o_lat [B,s_q,H,d_c] fp32.  out [B,s_q,H,d_v] fp32,

@@ -108,6 +108,8 @@ def test_null_pointers_rejected():
                                check=False) == mla.MLA_ERR_NULL
     assert mla.gqla_decode_step(s, f, f, f, f, f, f, f, f, None, stream=0,
                                 check=False) == mla.MLA_ERR_NULL
+    assert mla.mla_cache_append(s, 5120, 1e4, f, f, f, f, f, None, stream=0,
+                                check=False) == mla.MLA_ERR_NULL
     # a NULL shape pointer
     lib = mla.load()
     assert lib.mla_absorb_q(None, f, f, f, None) == mla.MLA_ERR_NULL
@@ -119,6 +121,19 @@ def test_combine_width_checked():
     assert mla.mla_splitkv_combine(s, 0, f, f, f, stream=0, check=False) == mla.MLA_ERR_SHAPE
     assert mla.mla_splitkv_combine(s, 2048, f, f, f, stream=0,
                                    check=False) == mla.MLA_ERR_UNSUPPORTED
+
+
+def test_cache_append_arguments_checked():
+    s = good_shape()
+    f = 0x1000
+    for d_model, base, status in ((0, 1e4, mla.MLA_ERR_SHAPE), (-8, 1e4, mla.MLA_ERR_SHAPE),
+                                  (5120, 0.0, mla.MLA_ERR_SHAPE),
+                                  (5120, float("nan"), mla.MLA_ERR_SHAPE),
+                                  (5124, 1e4, mla.MLA_ERR_UNSUPPORTED)):
+        assert mla.mla_cache_append(s, d_model, base, f, f, f, f, f, f, stream=0,
+                                    check=False) == status
+    assert mla.mla_cache_append(good_shape(batch=0), 5120, 1e4, f, f, f, f, f, f, stream=0,
+                                check=False) == mla.MLA_ERR_SHAPE
 
 
 def test_error_raises_with_check():

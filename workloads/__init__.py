@@ -6,4 +6,4 @@ arithmetic: only random draws, the paged-cache layout (page permutation, padding
 the bf16 encoding of the drawn values.
 """
 from .configs import CONFIGS, Config, get_config  # noqa: F401
-from .gen import make_inputs, bf16_round, Inputs  # noqa: F401
+from .gen import make_inputs, make_append_inputs, bf16_round, Inputs  # noqa: F401

@@ -8,6 +8,8 @@ Recipe (seed s, numpy ``SeedSequence(s).spawn(7)`` streams in this order):
   4 W_UV     ~ N(0, 1) / sqrt(d_c)             [H_w, d_v, d_c]
   5 ctx_lens fixed, or integer-uniform in [lo, hi] inclusive
   6 page permutation of all used pages
+The cache-append step's inputs (hidden states, W_DKV, W_KR) come from
+``make_append_inputs`` with streams of their own.
 Values are drawn in float32; for bf16 workloads they are rounded to bf16
 (round-to-nearest-even) and those bf16 values ARE the inputs.  The pool is generated in
 physical page order; sequence b owns ceil(T_b / P) pages whose physical ids are
@@ -158,3 +160,30 @@ def make_inputs(cfg: Config, seed=None, identity_table=False, extra_pages=0,
             pool[perm[off + n - 1], tail:] = nan
         off += n
     return Inputs(cfg, q, w_uk, w_uv, pool, table, ctx)
+
+
+class AppendInputs:
+    """Inputs of the cache-append step for one workload: the new tokens' hidden states
+    and the two down-projections (float32; bf16-exact for bf16 workloads)."""
+
+    def __init__(self, h, w_dkv, w_kr):
+        self.h, self.w_dkv, self.w_kr = h, w_dkv, w_kr
+        self.d_model = h.shape[-1]
+
+
+def make_append_inputs(cfg: Config, d_model=5120, seed=None):
+    """Seeded inputs of the cache-append step, from streams of their own
+    (``SeedSequence([seed, 1]).spawn(3)``) so the decode inputs of the same seed are
+    unchanged:  0 h ~ N(0, 1) [B, s_q, d_model];  1 W_DKV ~ N(0, 1) / sqrt(d_model)
+    [d_c, d_model];  2 W_KR ~ N(0, 1) / sqrt(d_model) [d_rope, d_model].  The
+    projections then have unit variance, like the drawn cache rows."""
+    seed = cfg.seed if seed is None else seed
+    streams = [np.random.default_rng(x) for x in np.random.SeedSequence([seed, 1]).spawn(3)]
+    bf16 = cfg.dtype == "bf16"
+    inv = np.float32(1.0 / np.sqrt(d_model))
+    h = _normal(streams[0], (cfg.batch, cfg.s_q, d_model), bf16)
+    w_dkv = _normal(streams[1], (cfg.d_c, d_model), False) * inv
+    w_kr = _normal(streams[2], (cfg.d_rope, d_model), False) * inv
+    if bf16:
+        w_dkv, w_kr = bf16_round(w_dkv), bf16_round(w_kr)
+    return AppendInputs(h, w_dkv, w_kr)
