@@ -7,7 +7,8 @@
 // rotary embedding's own definition.
 //
 // A weight-read-bound GEMV: W_DKV and W_KR (D x d_model) are read once per block of
-// tokens; the hidden states are small and come from L2.
+// tokens; the hidden states are small and come from L2.  bf16 runs on the matrix cores,
+// fp32 (and shapes the matrix-core kernel does not take) on the vector units.
 #include <math.h>
 
 #include "common.hpp"
@@ -116,6 +117,86 @@ __global__ __launch_bounds__(kApThreads) void cache_append_kernel(
   stf(pool + (static_cast<size_t>(page) * P + t % P) * D + o, v);
 }
 
+// bf16 on the matrix cores: out[row][token] = sum_k W[row][k] h[token][k] as
+// v_mfma_f32_16x16x32_bf16 with the weight rows as the A operand and the hidden states as
+// the B operand, both read in their natural row-major layout (K = d_model contiguous).
+// Block (16 output rows, 16 tokens), 8 waves splitting the K-steps; the partial products
+// meet in LDS in wave order.  Lane l of the result holds rows 4 (l / 16) + j, j < 4, of
+// token l % 16, so both rows of a RoPE pair are in one lane.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kApmWaves = 8;
+constexpr int kApmBatch = 10;   // K-steps whose loads are in flight together
+
+__global__ __launch_bounds__(64 * kApmWaves) void cache_append_mfma_kernel(
+    const bf16_t* __restrict__ h, const bf16_t* __restrict__ w_dkv,
+    const bf16_t* __restrict__ w_kr, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ ctx_lens, bf16_t* __restrict__ pool, int NQ, int s_q,
+    int d_c, int d_r, int d_model, int max_pages, int num_pages, int P, double log_base) {
+  __shared__ f32x4_t red[kApmWaves - 1][64];
+  const int D = d_c + d_r;
+  const int o0 = 16 * blockIdx.x, n0 = 16 * blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 15, kg = lane >> 4;
+  const int o = o0 + m;                       // D is a multiple of 16: always a real row
+  const bf16_t* wr = (o < d_c ? w_dkv + static_cast<size_t>(o) * d_model
+                              : w_kr + static_cast<size_t>(o - d_c) * d_model) + 8 * kg;
+  const bool tok_ok = n0 + m < NQ;
+  const bf16_t* hr = h + static_cast<size_t>(min(n0 + m, NQ - 1)) * d_model + 8 * kg;
+  const int n_k = d_model / 32;
+  const int per = (n_k + kApmWaves - 1) / kApmWaves;
+  const int kb = wave * per, ke = min(n_k, kb + per);
+  f32x4_t acc = {};
+  for (int k0 = kb; k0 < ke; k0 += kApmBatch) {
+    uint4 a[kApmBatch], b[kApmBatch];
+#pragma unroll
+    for (int t = 0; t < kApmBatch; ++t) {
+      const int ks = min(k0 + t, ke - 1);
+      a[t] = *reinterpret_cast<const uint4*>(wr + 32 * ks);
+      b[t] = *reinterpret_cast<const uint4*>(hr + 32 * ks);
+    }
+    // predicated, not a break: the loop must unroll fully so a[] and b[] stay in registers
+#pragma unroll
+    for (int t = 0; t < kApmBatch; ++t) {
+      const uint4 bv = tok_ok ? b[t] : make_uint4(0u, 0u, 0u, 0u);
+      if (k0 + t < ke)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[t]),
+                                                      __builtin_bit_cast(bf16x8_t, bv), acc,
+                                                      0, 0, 0);
+    }
+  }
+  if (wave > 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kApmWaves - 1; ++w) acc += red[w][lane];
+  // lane: token n0 + lane % 16, rows o0 + 4 (lane / 16) + j
+  const int q = n0 + (lane & 15);
+  if (q >= NQ) return;
+  const int b = q / s_q, s = q - b * s_q;
+  const int t = ctx_lens[b] - s_q + s;
+  if (t < 0 || t / P >= max_pages) return;
+  const int page = page_table[static_cast<size_t>(b) * max_pages + t / P];
+  if (page < 0 || page >= num_pages) return;
+  bf16_t* dst = pool + (static_cast<size_t>(page) * P + t % P) * D + o0 + 4 * (lane >> 4);
+  const int ob = o0 + 4 * (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < 4; j += 2) {
+    float x0 = acc[j], x1 = acc[j + 1];
+    if (ob + j >= d_c) {   // a RoPE pair: rows ob + j (even) and ob + j + 1
+      const int i = (ob + j - d_c) >> 1;
+      const double ang = static_cast<double>(t) * exp(-log_base * (2.0 * i) / d_r);
+      const double c = cos(ang), sn = sin(ang);
+      const float y0 = static_cast<float>(x0 * c - x1 * sn);
+      const float y1 = static_cast<float>(x0 * sn + x1 * c);
+      x0 = y0;
+      x1 = y1;
+    }
+    dst[j] = f32_to_bf16(x0);
+    dst[j + 1] = f32_to_bf16(x1);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_cache_append(const mla_shape_t& s, int d_model, float rope_base,
@@ -125,6 +206,14 @@ hipError_t launch_cache_append(const mla_shape_t& s, int d_model, float rope_bas
   const int NQ = s.batch * s.s_q, D = s.d_c + s.d_rope;
   const dim3 grid((D + kApRows - 1) / kApRows, (NQ + kApTok - 1) / kApTok);
   const double lb = log(static_cast<double>(rope_base));
+  if (s.dtype == MLA_BF16 && D % 16 == 0 && d_model % 32 == 0) {
+    hipLaunchKernelGGL(cache_append_mfma_kernel, dim3(D / 16, (NQ + 15) / 16),
+                       dim3(64 * kApmWaves), 0, st, static_cast<const bf16_t*>(h),
+                       static_cast<const bf16_t*>(w_dkv), static_cast<const bf16_t*>(w_kr),
+                       page_table, ctx_lens, static_cast<bf16_t*>(pool), NQ, s.s_q, s.d_c,
+                       s.d_rope, d_model, s.max_pages, s.num_pages, s.page_size, lb);
+    return hipGetLastError();
+  }
   if (s.dtype == MLA_F32)
     hipLaunchKernelGGL(cache_append_kernel<float>, grid, dim3(kApThreads), 0, st,
                        static_cast<const float*>(h), static_cast<const float*>(w_dkv),

@@ -93,6 +93,14 @@ def test_bf16_append_dsv2_shapes(s_q, ctx):
     check_append(inp, make_append_inputs(cfg, seed=32))
 
 
+def test_bf16_append_vector_path():
+    """A hidden width that is a multiple of 8 but not of 32 takes the vector-unit kernel
+    (the matrix-core one needs whole 32-wide K-steps)."""
+    cfg = get_config("dsv2-b16-t4096", batch=3, s_q=2, ctx=("list", [1, 64, 3000]))
+    inp = make_inputs(cfg, seed=36)
+    check_append(inp, make_append_inputs(cfg, d_model=200, seed=36))
+
+
 def test_bf16_append_gqla_shape():
     cfg = get_config("gqla-b32-t8192", batch=3, ctx=("list", [5, 700, 65536]))
     inp = make_inputs(cfg, seed=33)
