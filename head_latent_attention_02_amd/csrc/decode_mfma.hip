@@ -15,9 +15,9 @@
 // O^T[latent][row] += C_tile^T . P^T over the tile's 32 tokens.  Per 32-token tile ("slot"
 // s, one workgroup barrier each):
 //  * The two value waves stream the chunk through a 4-deep LDS ring: each loads half of
-//    tile s+2 into registers during slot s (buffer loads; the buffer's size is the tile's
+//    tile s+3 into registers during slot s (buffer loads; the buffer's size is the tile's
 //    valid rows, so rows past the chunk end read as zeros) and stores it at the start of
-//    slot s+1.  They then multiply tile s-2, reading it transposed with ds_read_b64_tr_b16
+//    slot s+2, so a load has two slots to land (two register buffers alternate).  They then multiply tile s-2, reading it transposed with ds_read_b64_tr_b16
 //    as the A operand; O^T lives in AGPRs (256 latent columns x 32 NQ rows per wave).
 //  * The score waves (32 rows each, q_abs held in registers as the B operand) issue the 36
 //    MFMAs of tile s and, between them, the softmax of tile s-1 in small pieces that issue
@@ -156,10 +156,14 @@ __device__ __forceinline__ void load_stage(Stage<kLoads>& st,
 template <int NL>
 __device__ __forceinline__ void store_stage(Smem& sm, const Stage<NL>& st, int lane, int kt,
                                             int first, int stride) {
-  char* dst = &sm.ring[kt & (kNB - 1)][0];
+  // the per-lane part of the address is formed here, at each use: a copy kept live
+  // across the whole pass gets spilled, and its reload would wait on every load in flight
+  int lofs = lane * 16 + first * 1024;
+  asm volatile("" : "+v"(lofs));
+  char* dst = &sm.ring[kt & (kNB - 1)][0] + lofs;
 #pragma unroll
   for (int j = 0; j < NL; ++j)
-    *reinterpret_cast<u32x4*>(dst + (first + stride * j) * 1024 + lane * 16) = st.r[j];
+    *reinterpret_cast<u32x4*>(dst + stride * j * 1024) = st.r[j];
 }
 
 __device__ __forceinline__ float xhalf_max(float v) {
@@ -279,7 +283,10 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
   f32x16 sacc[2];
   bool restarted = false;
   // one slot; P = parity of s (sacc[P] takes tile s, sacc[1 - P] holds tile s-1).
-  // Returns true when the pass is over (last slot done, or a rerun).
+  // Slots run in turns of two (even, odd) and every wave acts on a rerun request or the
+  // end of the pass only at the end of a turn, so the value waves' loop has a single
+  // exit; a turn may run one slot past n + 1, which does no work.
+  // Returns true when the pass is over (at an odd slot: last slot done, or a rerun).
   auto slot = [&](auto par, int s) -> bool {
     constexpr int P = decltype(par)::value;
     const long long seen = (s >= 2) ? sm.flag[s & 1] : -1;   // tile s-2's request
@@ -306,14 +313,14 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
     const bool rerun = s >= 2 && seen == rerun_tag(reruns, s - 2);
     __syncthreads();
     if (rerun) restarted = true;
-    return rerun || s == n + 1;
+    return P == 1 && (restarted || s >= n + 1);
   };
   while (true) {
     l_run = 0.f;
     restarted = false;
     __syncthreads();   // the value waves have stored tile 0
     for (int s = 0;; s += 2) {
-      if (slot(std::integral_constant<int, 0>(), s)) break;
+      slot(std::integral_constant<int, 0>(), s);
       if (slot(std::integral_constant<int, 1>(), s + 1)) break;
     }
     if (!restarted) break;
@@ -335,12 +342,16 @@ __device__ __forceinline__ void value_ring_tile(Smem& sm, int slot, int pb_i,
                                                 const int (&trofs)[2][2][2], int n32, int g,
                                                 f32x16 (&acc)[8][NQ]) {
   bf16x8 pb[2][NQ];
+  // per-lane offset formed at each use (see store_stage): the constant parts fold into
+  // the LDS instructions' offset field
+  int pofs = n32 * kPRow + 8 * g;
+  asm volatile("" : "+v"(pofs));
+  const bf16_t* pbase = &sm.pbuf[pb_i][0] + pofs;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int nb = 0; nb < NQ; ++nb)
-      pb[kt][nb] = *reinterpret_cast<const bf16x8*>(
-          &sm.pbuf[pb_i][(32 * nb + n32) * kPRow + 16 * kt + 8 * g]);
+      pb[kt][nb] = *reinterpret_cast<const bf16x8*>(pbase + 32 * nb * kPRow + 16 * kt);
   const char* cb = &sm.ring[slot][0];
   // the 8 base offsets, opaque per tile, so that their per-block variants are formed
   // here (one add each) rather than kept live across the loop
@@ -409,11 +420,12 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
         trofs[par][kt][h4] = tok * kRowB + (((col >> 3) ^ rswz(tok)) * 16) + (col & 7) * 2;
       }
   const int n = w.n_tiles;
-  // this wave streams 1-KB blocks VW, VW + 2, ... of every tile.  Tile s+1 is loaded into
-  // registers during slot s-1 and stored into the ring at the start of slot s (its ring
-  // slot held tile s-3, last read by the value waves in slot s-1), so every load has a
-  // whole slot to land.  Slot s multiplies tile s-2 (its P was published in slot s-1).
-  Stage<kLoads> stg;
+  // this wave streams 1-KB blocks VW, VW + 2, ... of every tile, two tiles ahead: tile
+  // s+1 is loaded into registers during slot s-2 and stored into the ring at the start of
+  // slot s (its ring slot held tile s-3, last read by the value waves in slot s-1), so
+  // every load has two whole slots to land.  Two register buffers alternate: tile t lives
+  // in stg[t & 1].  Slot s multiplies tile s-2 (its P was published in slot s-1).
+  Stage<kLoads> stg[2];
   uint32_t (&plan)[kLoads / 2][64] = sm.plan[VW];
   make_plan(plan, lane, VW);
   int reruns = 0;
@@ -421,19 +433,21 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
     // Loads and stores are unconditional: past the last tile they repeat tile n-1 into
     // ring slot (s+1) % 4, which no wave reads in slot s and no later slot needs.
     const int last = max(n - 1, 0);
-    // prologue: tile 0 in the ring, tile 1 in registers
-    load_stage(stg, plan, w, 0, lane);
-    store_stage(sm, stg, lane, 0, VW, 2);
-    load_stage(stg, plan, w, min(1, last), lane);
+    // prologue: tile 0 in the ring, tiles 1 and 2 in registers
+    load_stage(stg[0], plan, w, 0, lane);
+    load_stage(stg[1], plan, w, min(1, last), lane);
+    store_stage(sm, stg[0], lane, 0, VW, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(stg[0], plan, w, min(2, last), lane);
     __syncthreads();
     // slots 0 and 1: the score waves start; tiles 1 and 2 go into the ring
-    store_stage(sm, stg, lane, 1, VW, 2);
+    store_stage(sm, stg[1], lane, 1, VW, 2);
     __builtin_amdgcn_sched_barrier(0);
-    load_stage(stg, plan, w, min(2, last), lane);
+    load_stage(stg[1], plan, w, min(3, last), lane);
     __syncthreads();
-    store_stage(sm, stg, lane, 2, VW, 2);
+    store_stage(sm, stg[0], lane, 2, VW, 2);
     __builtin_amdgcn_sched_barrier(0);
-    load_stage(stg, plan, w, min(3, last), lane);
+    load_stage(stg[0], plan, w, min(4, last), lane);
     __syncthreads();
     if (n == 0) {
       __syncthreads();   // the score waves have published the row sums
@@ -444,25 +458,40 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
               make_float4(0.f, 0.f, 0.f, 0.f);
       return;
     }
-    // slot 2 (peeled, so the accumulators are first written outside the loop)
+    // slot s stores tile s+1 from stg[(s+1) & 1], reloads that buffer with tile s+3 and
+    // multiplies tile s-2 (none past the last tile: a turn can run one slot past n+1)
     f32x16 acc[8][NQ];
-    long long seen = sm.flag[0];
-    store_stage(sm, stg, lane, 3, VW, 2);
+    long long seen;
+    bool restarted = false;
+    auto vslot = [&](auto par, int s) {
+      constexpr int X = decltype(par)::value;   // (s + 1) & 1
+      seen = sm.flag[s & 1];
+      store_stage(sm, stg[X], lane, s + 1, VW, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(stg[X], plan, w, min(s + 3, last), lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s - 2 < n)
+        value_ring_tile<NQ, false>(sm, (s - 2) & (kNB - 1), (s - 2) & 1, trofs, n32, g, acc);
+      restarted |= seen == rerun_tag(reruns, s - 2);
+      __syncthreads();
+    };
+    // turn (2, 3); slot 2 is peeled so the accumulators are first written outside the loop
+    seen = sm.flag[0];
+    store_stage(sm, stg[1], lane, 3, VW, 2);
     __builtin_amdgcn_sched_barrier(0);
-    load_stage(stg, plan, w, min(4, last), lane);
+    load_stage(stg[1], plan, w, min(5, last), lane);
     __builtin_amdgcn_sched_barrier(0);
     value_ring_tile<NQ, true>(sm, 0, 0, trofs, n32, g, acc);
-    bool restarted = seen == rerun_tag(reruns, 0);
+    restarted = seen == rerun_tag(reruns, 0);
     __syncthreads();
-    for (int s = 3; s <= n + 1 && !restarted; ++s) {
-      seen = sm.flag[s & 1];
-      store_stage(sm, stg, lane, s + 1, VW, 2);
-      __builtin_amdgcn_sched_barrier(0);
-      load_stage(stg, plan, w, min(s + 2, last), lane);
-      __builtin_amdgcn_sched_barrier(0);
-      value_ring_tile<NQ, false>(sm, (s - 2) & (kNB - 1), (s - 2) & 1, trofs, n32, g, acc);
-      restarted = seen == rerun_tag(reruns, s - 2);
-      __syncthreads();
+    vslot(std::integral_constant<int, 0>(), 3);
+    // turns (4, 5), (6, 7), ...: the pass ends after the turn holding slot n + 1
+    if (!restarted && n + 1 > 3) {
+      for (int s = 4;; s += 2) {
+        vslot(std::integral_constant<int, 1>(), s);
+        vslot(std::integral_constant<int, 0>(), s + 1);
+        if (restarted || s + 1 >= n + 1) break;
+      }
     }
     if (restarted) {
       ++reruns;
