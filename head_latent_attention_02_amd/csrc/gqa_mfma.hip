@@ -20,8 +20,11 @@
 //    ds_read_b64_tr_b16 as the A operand of O^T += V^T P^T.  P comes straight from the
 //    score accumulators: the token order of the value product is permuted to match the
 //    score layout, so P never leaves the lane that computed it.
-//  * The next tile's 20 loads per lane are in flight while the current tile computes
-//    (two register tiles, ping-pong, loads always issued so the wait counts stay exact).
+//  * Latency is hidden across waves rather than inside one: the LDS (80 KB, the tiles and
+//    the final merge buffers share it) and the registers (under 256) fit two workgroups,
+//    8 waves, per CU, so while one wave waits for its tile the others compute.  (A
+//    register ping-pong of two tiles per wave needs ~435 registers and allows one
+//    workgroup per CU; it measured 2-3 % slower.)
 //  * Workgroups of one (b, u) sit 8 apart in the grid so that all groups of a chunk run
 //    on one XCD and share its L2 for the k^R rows.
 // Rows past the chunk end are loaded from the tile's first token (valid data) and
@@ -75,13 +78,16 @@ struct Args {
   int G, j, lo, hi;
 };
 
+struct Red {
+  float o[kWaves][kMaxRows][kDV];   // per-wave O, after the loop
+  float m[kWaves][32];
+  float l[kWaves][32];
+};
 struct Smem {
   union {
-    WaveTile tile[kWaves];                      // per-wave row tiles
-    float red_o[kWaves][kMaxRows][kDV];         // per-wave O, after the loop
+    WaveTile tile[kWaves];   // per-wave row tiles
+    Red red;                 // after the loop (80 KB in all: two workgroups per CU)
   };
-  float red_m[kWaves][32];
-  float red_l[kWaves][32];
 };
 
 // chunk swizzles: keys and RoPE keys are read 16 tokens x one chunk at a time, values
@@ -209,7 +215,7 @@ __device__ __forceinline__ void process_tile(const Tile& tl, const bf16x8 (&qn)[
     }
 }
 
-__global__ __launch_bounds__(256, 1) void gqa_decode_mfma_kernel(
+__global__ __launch_bounds__(256, 2) void gqa_decode_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kpool,
     const bf16_t* __restrict__ vpool, const bf16_t* __restrict__ krpool,
     const int32_t* __restrict__ pt, const int32_t* __restrict__ lens,
@@ -275,52 +281,40 @@ __global__ __launch_bounds__(256, 1) void gqa_decode_mfma_kernel(
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x16{};
 
-  if (wave < n_tiles) {
-    Tile A, B;
-    load_tile(A, a, a.lo + wave * kTT, lane);
-    // the scheduling barriers keep every load of the next tile ahead of the first use of
-    // the current one, so a whole tile is always in flight
-    for (int k = wave;; k += 2 * kWaves) {
-      load_tile(B, a, a.lo + min(k + kWaves, n_tiles - 1) * kTT, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      process_tile(A, qn, qr, wt, rdo, row_lim - (a.lo + k * kTT), zscale, lane, st, acc);
-      if (k + kWaves >= n_tiles) break;
-      load_tile(A, a, a.lo + min(k + 2 * kWaves, n_tiles - 1) * kTT, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      process_tile(B, qn, qr, wt, rdo, row_lim - (a.lo + (k + kWaves) * kTT), zscale, lane,
-                   st, acc);
-      if (k + 2 * kWaves >= n_tiles) break;
-    }
+  for (int k = wave; k < n_tiles; k += kWaves) {
+    Tile A;
+    load_tile(A, a, a.lo + k * kTT, lane);
+    process_tile(A, qn, qr, wt, rdo, row_lim - (a.lo + k * kTT), zscale, lane, st, acc);
   }
 
   // merge the 4 waves: each writes its O into the LDS the tiles used
   __syncthreads();
   const float l_tot = xhalf_sum(st.l);
   if (g == 0) {
-    sm.red_m[wave][n] = st.m;
-    sm.red_l[wave][n] = l_tot;
+    sm.red.m[wave][n] = st.m;
+    sm.red.l[wave][n] = l_tot;
   }
   if (n < R) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        sm.red_o[wave][n][32 * mb + 8 * (e >> 2) + 4 * g + (e & 3)] = acc[mb][e];
+        sm.red.o[wave][n][32 * mb + 8 * (e >> 2) + 4 * g + (e & 3)] = acc[mb][e];
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < R * kDV; idx += blockDim.x) {
     const int r = idx / kDV, c = idx - r * kDV;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.red_m[w][r]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.red.m[w][r]);
     float o = 0.f, lsum = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float mw = sm.red_m[w][r];
+        const float mw = sm.red.m[w][r];
         const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-        lsum += f * sm.red_l[w][r];
-        o += f * sm.red_o[w][r][c];
+        lsum += f * sm.red.l[w][r];
+        o += f * sm.red.o[w][r][c];
       }
     }
     const int s = r / hg, h = j * hg + (r - s * hg);
