@@ -387,13 +387,16 @@ __global__ __launch_bounds__(64 * kUvmWaves) void out_uv_mfma_kernel(
 
 // ---------------------------------------------------------------- a3 + a4 fused
 // The step's split merge and value up-projection in one launch (bf16 weights, d_c = 512,
-// d_v = 128, at most 64 splits).  Block (head h, 32 queries), 8 waves.  Arithmetic is the
+// d_v = 128, at most 64 splits, heads a multiple of 8).  Block (head h, half of its 128
+// value rows, 32 queries), 8 waves; the two halves of a head are 8 blocks apart, so they
+// run on one XCD and the second one's partial reads hit its L2.  Arithmetic is the
 // same, operation for operation, as combine_kernel followed by out_uv_mfma_kernel, so the
 // results are bitwise those of the two separate entry points; what changes is that the
 // merged latent rows go to the up-projection through LDS and that the weight loads, the
 // partial loads and the lse reductions are all in flight together.
-//   wave w: value rows 32 (w % 4) .. +32 and latent quarters 2 (w / 4), 2 (w / 4) + 1 of
-//   the up-projection; all waves share the merge (4 queries x 512 columns per pass).
+//   wave w: value rows 64 half + 32 (w % 2) .. +32 and latent quarter w / 2 of the
+//   up-projection; all waves share the merge (4 queries x 512 columns per pass), which
+//   both halves compute (only half 0 stores o_lat and lse).
 constexpr int kFuQ = 32;          // queries per block
 constexpr int kFuBatch = 16;      // partial loads per thread in flight at once
 constexpr int kFuRow = 512 + 8;   // bf16 elements per LDS row of merged latents (padded)
@@ -406,20 +409,23 @@ __global__ __launch_bounds__(512) void combine_out_uv_kernel(
   __shared__ __align__(16) bf16_t ob[kFuQ * kFuRow];   // merged latents as MFMA B rows
   __shared__ float wts[kFuQ][64];                       // chunk weights e^{lse_u - max}
   __shared__ float inv_s[kFuQ];
-  __shared__ float red[4][2][16][64];                   // quarters 2, 3 per value block
-  const int h = blockIdx.x, q0 = blockIdx.y * kFuQ;
+  __shared__ float red[2][3][16][64];                   // quarters 1-3 per value block
+  const int hx = blockIdx.x;
+  const int h = (hx >> 4) * 8 + (hx & 7), half = (hx >> 3) & 1;
+  const int q0 = blockIdx.y * kFuQ;
   const int nqb = min(kFuQ, NQ - q0);
   const int w = h / (H / Hw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m = lane & 31, g = lane >> 5, vb = wave & 3, kh = wave >> 2;
+  const int m = lane & 31, g = lane >> 5, vb = wave & 1, kq = wave >> 1;
+  const int v0 = 64 * half + 32 * vb;   // this wave's first value row
 
-  // (1) this wave's weight rows: 16 K-steps of 16 latent columns, all in flight
-  uint4 a[16];
+  // (1) this wave's weight rows: its quarter's 8 K-steps of 16 latent columns, in flight
+  uint4 a[8];
   {
-    const bf16_t* wr = w_uv + (static_cast<size_t>(w) * d_v + 32 * vb + m) * d_c + 8 * g;
+    const bf16_t* wr = w_uv + (static_cast<size_t>(w) * d_v + v0 + m) * d_c + 8 * g;
 #pragma unroll
-    for (int t = 0; t < 16; ++t)
-      a[t] = *reinterpret_cast<const uint4*>(wr + 16 * (16 * kh + t));
+    for (int t = 0; t < 8; ++t)
+      a[t] = *reinterpret_cast<const uint4*>(wr + 16 * (8 * kq + t));
   }
   // (2) the first batch of partials of merge pass 0
   const int cq = tid >> 7, c4 = 4 * (tid & 127);
@@ -448,8 +454,9 @@ __global__ __launch_bounds__(512) void combine_out_uv_kernel(
       }
       tot = wave_sum(tot);
       inv = 1.f / tot;
-      if (lane == 0 && lse) lse[static_cast<size_t>(q0 + n) * H + h] = mx + logf(tot);
-    } else if (lane == 0 && lse && n < nqb) {
+      if (lane == 0 && lse && half == 0)
+        lse[static_cast<size_t>(q0 + n) * H + h] = mx + logf(tot);
+    } else if (lane == 0 && lse && n < nqb && half == 0) {
       lse[static_cast<size_t>(q0 + n) * H + h] = -INFINITY;
     }
     wts[n][lane] = e;
@@ -475,7 +482,9 @@ __global__ __launch_bounds__(512) void combine_out_uv_kernel(
       }
       const float inv = inv_s[n];
       acc = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-      *reinterpret_cast<float4*>(o_lat + (static_cast<size_t>(q0 + n) * H + h) * d_c + c4) = acc;
+      if (half == 0)
+        *reinterpret_cast<float4*>(o_lat + (static_cast<size_t>(q0 + n) * H + h) * d_c + c4) =
+            acc;
     }
     const uint32_t bx = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc.x));
     const uint32_t by = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc.y));
@@ -484,36 +493,30 @@ __global__ __launch_bounds__(512) void combine_out_uv_kernel(
     *reinterpret_cast<uint2*>(ob + n * kFuRow + c4) = make_uint2(bx | (by << 16), bz | (bw << 16));
   }
   __syncthreads();
-  // (5) up-projection: two latent quarters per wave, each accumulated from zero
-  f32x16_t acc2[2] = {{}, {}};
+  // (5) up-projection: one latent quarter per wave, accumulated from zero
+  f32x16_t acc2 = {};
 #pragma unroll
-  for (int qq = 0; qq < 2; ++qq)
+  for (int t = 0; t < 8; ++t) {
+    const int ks = 8 * kq + t;
+    const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(ob + m * kFuRow + 16 * ks + 8 * g);
+    acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[t]), bv,
+                                                   acc2, 0, 0, 0);
+  }
+  if (kq > 0) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int ks = 16 * kh + 8 * qq + t;
-      const bf16x8_t bv =
-          *reinterpret_cast<const bf16x8_t*>(ob + m * kFuRow + 16 * ks + 8 * g);
-      acc2[qq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          __builtin_bit_cast(bf16x8_t, a[8 * qq + t]), bv, acc2[qq], 0, 0, 0);
-    }
-  if (kh == 1) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      red[vb][0][j][lane] = acc2[0][j];
-      red[vb][1][j][lane] = acc2[1][j];
-    }
+    for (int j = 0; j < 16; ++j) red[vb][kq - 1][j][lane] = acc2[j];
   }
   __syncthreads();
   // lane (query m, half g) holds value rows 8 (j / 4) + 4 g + j % 4 of block vb; the
   // quarters are summed in order 0, 1, 2, 3
-  if (kh == 0 && m < nqb) {
-    float* orow = out + (static_cast<size_t>(q0 + m) * H + h) * d_v + 32 * vb;
+  if (kq == 0 && m < nqb) {
+    float* orow = out + (static_cast<size_t>(q0 + m) * H + h) * d_v + v0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      float t = acc2[0][j];
-      t += acc2[1][j];
+      float t = acc2[j];
       t += red[vb][0][j][lane];
       t += red[vb][1][j][lane];
+      t += red[vb][2][j][lane];
       orow[8 * (j >> 2) + 4 * g + (j & 3)] = t;
     }
   }
@@ -655,15 +658,16 @@ hipError_t launch_out_uv(const mla_shape_t& s, const float* o_lat, const void* w
 }
 
 bool combine_out_uv_supported(const mla_shape_t& s) {
-  return s.dtype == MLA_BF16 && s.d_c == 512 && s.d_v == 128 && s.n_splits <= 64;
+  return s.dtype == MLA_BF16 && s.d_c == 512 && s.d_v == 128 && s.n_splits <= 64 &&
+         s.n_heads % 8 == 0;
 }
 
 hipError_t launch_combine_out_uv(const mla_shape_t& s, const float* o_part,
                                  const float* lse_part, const void* w_uv, float* o_lat,
                                  float* lse, float* out, hipStream_t st) {
   const int NQ = s.batch * s.s_q;
-  hipLaunchKernelGGL(combine_out_uv_kernel, dim3(s.n_heads, (NQ + kFuQ - 1) / kFuQ), dim3(512),
-                     0, st, o_part, lse_part, static_cast<const bf16_t*>(w_uv), o_lat, lse,
+  hipLaunchKernelGGL(combine_out_uv_kernel, dim3(2 * s.n_heads, (NQ + kFuQ - 1) / kFuQ),
+                     dim3(512), 0, st, o_part, lse_part, static_cast<const bf16_t*>(w_uv), o_lat, lse,
                      out, NQ, s.n_heads, s.n_wheads, s.n_splits);
   return hipGetLastError();
 }

@@ -112,12 +112,14 @@ def test_tiny_f32_step_entry_point_matches_steps():
     ("dsv2-b16-t4096", 1, [5000, 64], 64),
     ("dsv2-b16-t4096", 2, [1, 2, 130], 1),
     ("gqla-b32-t8192", 2, [700, 64, 1999], 5),
+    ("gqla-shard-b32-t65536", 1, [700, 64, 1999], 3),
 ])
 def test_bf16_step_entry_point_matches_steps(name, s_q, ctx, S):
     """At bf16 with d_c 512 and d_v 128 the step entry point merges the splits and
     up-projects in one kernel; its outputs must equal those of the separate entry points
     bit for bit (20 sequences at s_q = 2 give two query blocks of 32, the second ragged;
-    s_q = 2 over one token gives rows with no visible token), and match the oracle."""
+    s_q = 2 over one token gives rows with no visible token; 4 heads take the separate
+    kernels inside the step), and match the oracle."""
     cfg = get_config(name, batch=len(ctx), s_q=s_q, ctx=("list", ctx))
     inp = make_inputs(cfg, seed=21)
     announce(f"case {name} s_q={s_q} ctx={ctx[:6]} S={S}")
