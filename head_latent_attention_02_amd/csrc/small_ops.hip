@@ -53,12 +53,14 @@ __device__ __forceinline__ void to_f32(const Raw8<float>& r, float (&x)[8]) {
 }
 
 // ---------------------------------------------------------------- a1 absorb
-// Block (head h, 256 latent columns, QB = 4 or 8 queries), 256 threads.  Thread
-// (rs, cl) = (tid / 32, tid % 32) owns columns c0 + 8 cl .. +8 and weight rows rs, rs + 8,
-// ...: each W_UK row chunk is one 512-byte coalesced read per 32 lanes, and every weight
-// byte of the block is read once.
-constexpr int kAbsCols = 256;
-constexpr int kAbsBatch = 16;   // weight rows per thread in flight at once
+// Block (head h, 128 latent columns, QB = 4 or 8 queries), 256 threads: 512 blocks at
+// 128 heads, two per CU.  Thread (rs, cl) = (tid / 16, tid % 16) owns columns
+// c0 + 8 cl .. +8 and weight rows rs, rs + 16, ...: each W_UK row chunk is one 256-byte
+// coalesced read per 16 lanes, and every weight byte of the block is read once.
+constexpr int kAbsLanes = 16;                  // lanes per weight row chunk
+constexpr int kAbsCols = 8 * kAbsLanes;        // 128 latent columns per block
+constexpr int kAbsSlices = 256 / kAbsLanes;    // 16 row slices
+constexpr int kAbsBatch = 8;   // weight rows per thread in flight at once
 template <typename T, int QB>
 __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
                                                        const T* __restrict__ w_uk,
@@ -71,17 +73,17 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
   const int w = h / (H / Hw);
   const int nq = min(QB, NQ - q0);
   const int dq = d_n + d_r, D = d_c + d_r;
-  const int tid = threadIdx.x, rs = tid >> 5, cl = tid & 31;
+  const int tid = threadIdx.x, rs = tid / kAbsLanes, cl = tid % kAbsLanes;
   const int c = c0 + 8 * cl;
   const T* W = w_uk + static_cast<size_t>(w) * d_n * d_c + c;
-  // weight rows rs, rs + 8, ... in batches of kAbsBatch: a batch's loads are all issued
+  // weight rows rs, rs + 16, ... in batches of kAbsBatch: a batch's loads are all issued
   // before any is used, and the first batch (at d_n = 128 a thread's whole share) before
   // the queries are staged, so the two reads overlap
   Raw8<T> raw[kAbsBatch];
   auto issue = [&](int i0) {
 #pragma unroll
     for (int bt = 0; bt < kAbsBatch; ++bt) {
-      const int i = i0 + 8 * bt;
+      const int i = i0 + kAbsSlices * bt;
       if (c < d_c && i < d_n) raw[bt] = load_raw8(W + static_cast<size_t>(i) * d_c);
     }
   };
@@ -103,11 +105,11 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[jq][e] = 0.f;
   if (c < d_c) {
-    for (int i0 = rs; i0 < d_n; i0 += 8 * kAbsBatch) {
+    for (int i0 = rs; i0 < d_n; i0 += kAbsSlices * kAbsBatch) {
       if (i0 != rs) issue(i0);
 #pragma unroll
       for (int bt = 0; bt < kAbsBatch; ++bt) {
-        const int i = i0 + 8 * bt;
+        const int i = i0 + kAbsSlices * bt;
         if (i >= d_n) break;
         float wv[8];
         to_f32(raw[bt], wv);
@@ -126,17 +128,20 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
       }
     }
   }
-  // the two row slices of a wave (lane halves) meet by a shuffle, the 4 waves in LDS
+  // the 4 row slices of a wave meet by shuffles, the 4 waves in LDS
 #pragma unroll
-  for (int jq = 0; jq < QB; ++jq)
+  for (int off = kAbsLanes; off < 64; off <<= 1)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[jq][e] += __shfl_xor(acc[jq][e], 32, 64);
-  if ((rs & 1) == 0) {
+    for (int jq = 0; jq < QB; ++jq)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[jq][e] += __shfl_xor(acc[jq][e], off, 64);
+  if ((tid & 63) < kAbsLanes) {
+    const int wv = tid >> 6;
 #pragma unroll
     for (int jq = 0; jq < QB; ++jq)
 #pragma unroll
       for (int e = 0; e < 8; e += 4)
-        *reinterpret_cast<float4*>(&red[((rs >> 1) * QB + jq) * kAbsCols + 8 * cl + e]) =
+        *reinterpret_cast<float4*>(&red[(wv * QB + jq) * kAbsCols + 8 * cl + e]) =
             make_float4(acc[jq][e], acc[jq][e + 1], acc[jq][e + 2], acc[jq][e + 3]);
   }
   __syncthreads();
