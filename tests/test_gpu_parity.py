@@ -196,6 +196,35 @@ def test_identity_vs_permuted_page_table_bitwise():
     assert torch.equal(out_perm, d2.out)
 
 
+def test_pages_above_4gib_bitwise():
+    """The same sequences with their pages moved past byte 4 GiB of a ~5.9 GB pool (page
+    ids from 80000, 73,728 bytes each) give bitwise the same step outputs: page and row
+    offsets are formed in 64 bits.  Every page below the moved ones is NaN."""
+    from workloads.device import shape_of
+    cfg = small(batch=2, ctx=("list", [700, 1100]))
+    a = make_inputs(cfg, seed=6)
+    d = DeviceInputs(a)
+    absorbed_step(d)
+    want, want_lse = d.out.clone(), d.lse.clone()
+    shift = 80000
+    big = torch.full((shift + a.num_pages, cfg.page_size, cfg.D), float("nan"),
+                     dtype=torch.bfloat16, device="cuda")
+    big[shift:] = d.pool
+    sh = shape_of(a)
+    sh.num_pages = shift + a.num_pages
+    table = torch.where(d.page_table >= 0, d.page_table + shift, d.page_table)
+    announce(f"case pages above 4 GiB: pool {big.numel() * 2 / 2**30:.2f} GiB")
+    op = d.o_part_view(cfg.d_c)
+    mla.mla_absorb_q(sh, d.q, d.w_uk, d.q_abs)
+    mla.mla_decode_absorbed(sh, d.q_abs, big, table, d.ctx_lens, op, d.lse_part)
+    mla.mla_splitkv_combine(sh, cfg.d_c, op, d.lse_part, d.o_lat, d.lse)
+    mla.mla_out_uv(sh, d.o_lat, d.w_uv, d.out)
+    torch.cuda.synchronize()
+    assert torch.equal(want, d.out) and torch.equal(want_lse, d.lse)
+    del big
+    torch.cuda.empty_cache()
+
+
 def test_deterministic_over_repeats():
     cfg = small(batch=2, ctx=("list", [1500, 900]))
     d = DeviceInputs(make_inputs(cfg, seed=6))
