@@ -356,7 +356,10 @@ def sampled_full_check(cfg, batches, heads, S=None, split_tokens=None):
     inp = make_inputs(cfg)
     announce(f"case full {cfg.name} tokens={inp.total_tokens} S={S or cfg.n_splits}")
     d = DeviceInputs(inp, n_splits=S, split_tokens=split_tokens)
-    absorbed_step(d)
+    # the step entry point, as the benchmark times it
+    mla.mla_decode_step(d.shape, d.q, d.w_uk, d.w_uv, d.pool, d.page_table, d.ctx_lens,
+                        d.q_abs, d.o_part, d.lse_part, d.o_lat, d.out, d.lse)
+    torch.cuda.synchronize()
     got = d.out.cpu().numpy()
     got_lse = d.lse.cpu().numpy()
     del d
@@ -384,12 +387,18 @@ def test_full_gqla_b32_t65536_absorbed():
     sampled_full_check(get_config("gqla-b32-t65536"), [0, 17, 31], list(range(32)))
 
 
+@pytest.mark.parametrize("name", ["gqla-b32-t8192", "gqla-b32-t16384", "gqla-b32-t32768"])
+def test_full_gqla_context_sweep_absorbed(name):
+    """The other points of the GQLA context sweep, at full size (32 sequences)."""
+    sampled_full_check(get_config(name), [0, 31], [0, 5, 13, 31])
+
+
 def test_full_mtp_b64_ragged():
     sampled_full_check(get_config("mtp-b64-ragged"), [0, 17, 40, 63], [0, 127, 77])
 
 
 @pytest.mark.parametrize("name", ["gqla-b32-t65536", "gqla-mtp-b32-t65536",
-                                  "gqla-shard-b32-t65536"])
+                                  "gqla-shard-b32-t65536", "gqla-b32-t8192"])
 def test_full_gqla_b32_t65536_gqa_path(name):
     """GQA path at its largest size: 32 sequences of 65536 tokens, expanded on the GPU; the
     same at s_q = 2 (two query rows per head, causal), and one rank's share under 8-way
