@@ -88,12 +88,12 @@ struct Smem {
   uint32_t plan[2][kLoads / 2][64];   // value wave VW's per-lane load offsets
 };
 
-// A score wave that must move a reference at tile k writes tag(pass, k) into flag[k & 1]
-// during slot k.  Every wave reads that word right after the barrier ending slot k and
-// acts on it at the barrier ending slot k+1: the word is stable during slot k+1 (the next
-// write to it is in slot k+2), so all waves agree without extra barriers, and tags of an
-// abandoned pass never match the next one.  The request is honoured one slot late, which
-// only wastes that slot's work.
+// The softmax of tile k runs in slot k+1; a score wave that must move a reference there
+// writes tag(pass, k) into flag[k & 1] during slot k+1.  Every wave reads that word at the
+// start of slot k+2 (after the barrier ending slot k+1), when it is stable (its next write
+// is in slot k+3), and acts on it at the end of the two-slot turn holding slot k+2, so all
+// waves agree without extra barriers; tags of an abandoned pass never match the next one.
+// The request is honoured one or two slots late, which only wastes those slots' work.
 __device__ __forceinline__ long long rerun_tag(int pass, int k) {
   return (static_cast<long long>(pass) << 32) | static_cast<unsigned>(k);
 }
