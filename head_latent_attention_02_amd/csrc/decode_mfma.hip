@@ -8,17 +8,22 @@
 // query the keys are never decompressed; AI Radio episode on GQLA, "Key concepts": on
 // the MQA-absorb path the latent is the shared key and value).
 //
-// One kernel, templated on NQ (1 or 2 score waves, i.e. 32 or 64 query rows per
-// workgroup; rows are the flattened (s, h) pairs).  One workgroup per (sequence b, chunk
-// u, row block), one per CU (~160 KB of LDS), NQ + 2 waves.  Both contractions run as
-// v_mfma_f32_32x32x16_bf16: S^T[token][row] = C_tile . q_abs^T over the 576-wide row, and
-// O^T[latent][row] += C_tile^T . P^T over the tile's 32 tokens.  Per 32-token tile ("slot"
-// s, one workgroup barrier each):
-//  * The two value waves stream the chunk through a 4-deep LDS ring: each loads half of
-//    tile s+3 into registers during slot s (buffer loads; the buffer's size is the tile's
-//    valid rows, so rows past the chunk end read as zeros) and stores it at the start of
-//    slot s+2, so a load has two slots to land (two register buffers alternate).  They then multiply tile s-2, reading it transposed with ds_read_b64_tr_b16
-//    as the A operand; O^T lives in AGPRs (256 latent columns x 32 NQ rows per wave).
+// Two kernels share the pipeline below.  One workgroup per (sequence b, chunk u, row
+// block), one per CU (~160 KB of LDS); rows are the flattened (s, h) pairs.  Blocks of 64
+// rows run eight waves, two per SIMD: two score waves (32 rows each), two loader waves that
+// only stream the chunk, and four value waves (128 latent columns each), placed so that
+// every SIMD carries about the same matrix work (36 or 32 MFMAs per slot) and has a second
+// wave to issue while the first waits.  Blocks of 32 rows (GQLA's absorbed shape) run three
+// waves, one per SIMD: one score wave and two value waves (256 columns each) that also
+// stream the chunk.  Both contractions run as v_mfma_f32_32x32x16_bf16: S^T[token][row] =
+// C_tile . q_abs^T over the 576-wide row, and O^T[latent][row] += C_tile^T . P^T over the
+// tile's 32 tokens.  Per 32-token tile ("slot" s, one workgroup barrier each):
+//  * The streaming waves keep a 4-deep LDS ring: each loads half of tile s+3 into
+//    registers during slot s (buffer loads; the buffer's size is the tile's valid rows, so
+//    rows past the chunk end read as zeros) and stores it at the start of slot s+2, so a
+//    load has two slots to land (two register buffers alternate).
+//  * The value waves multiply tile s-2, reading it transposed with ds_read_b64_tr_b16 as
+//    the A operand; O^T stays in the accumulators.
 //  * The score waves (32 rows each, q_abs held in registers as the B operand) issue the 36
 //    MFMAs of tile s and, between them, the softmax of tile s-1 in small pieces that issue
 //    while the matrix core is busy; P (bf16) goes to LDS for the value waves.
@@ -184,14 +189,14 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 // matrix core is busy (gfx950 hides about four VALU instructions behind each 32x32x16
 // MFMA; larger pieces stall it).  Lane (row n32, half g) holds tokens 8 (j / 4) + 4 g +
 // j % 4 of a tile; lim = visible tokens of its row there (MASK: some lane has lim < 32).
-template <bool DO_MFMA, bool DO_SOFT, bool MASK>
+template <bool DO_MFMA, bool DO_SOFT, bool MASK, int SPF = 8>
 __device__ __forceinline__ void score_slot(const char* tb, const bf16x8 (&qreg)[kKS],
                                            const int (&rb)[4], f32x16& sacc_out,
                                            const f32x16& sacc_in, int lim, float zscale,
                                            float slack, float& m_ref, float& l_run,
                                            bool& move, bf16_t* prow, int g) {
   // A operands run kPF K-steps ahead of the MFMA that consumes them
-  constexpr int kPF = 8;
+  constexpr int kPF = SPF;
   bf16x8 abuf[kPF];
   f32x16 acc = {};
   if (DO_MFMA) {
@@ -264,7 +269,7 @@ __device__ __forceinline__ void score_slot(const char* tb, const bf16x8 (&qreg)[
 
 // Score wave QW (rows 32 QW .. 32 QW + 31).  Slot s: the MFMAs of tile s and the softmax
 // (P, published to LDS) of tile s-1, so the value waves use tile s-2.
-template <int NQ, int QW>
+template <int NQ, int QW, int SPF = 8>
 __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
   const int n32 = lane & 31, g = lane >> 5;
   bf16x8 qreg[kKS];
@@ -297,16 +302,16 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
     bool move = false;
     const bool masked = __builtin_amdgcn_ballot_w64(lim < kTT) != 0;
     if (mf && sf && !masked)
-      score_slot<true, true, false>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
+      score_slot<true, true, false, SPF>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
                                     w.slack, m_ref, l_run, move, prow, g);
     else if (mf && sf)
-      score_slot<true, true, true>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
+      score_slot<true, true, true, SPF>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
                                    w.slack, m_ref, l_run, move, prow, g);
     else if (mf)
-      score_slot<true, false, false>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
+      score_slot<true, false, false, SPF>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
                                      w.slack, m_ref, l_run, move, prow, g);
     else if (sf)
-      score_slot<false, true, true>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
+      score_slot<false, true, true, SPF>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
                                     w.slack, m_ref, l_run, move, prow, g);
     if (sf && __builtin_amdgcn_ballot_w64(move) && reruns <= n)
       sm.flag[(s - 1) & 1] = rerun_tag(reruns, s - 1);
@@ -337,10 +342,10 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
 
 // One value-wave tile from ring slot `slot`: acc (+)= C^T . P^T.  The transposed
 // A-operand reads run four (mb, kt) steps ahead of their MFMA pair.
-template <int NQ, bool FIRST>
+template <int NQ, bool FIRST, int KMB = 8>
 __device__ __forceinline__ void value_ring_tile(Smem& sm, int slot, int pb_i,
                                                 const int (&trofs)[2][2][2], int n32, int g,
-                                                f32x16 (&acc)[8][NQ]) {
+                                                f32x16 (&acc)[KMB][NQ]) {
   bf16x8 pb[2][NQ];
   // per-lane offset formed at each use (see store_stage): the constant parts fold into
   // the LDS instructions' offset field
@@ -375,7 +380,7 @@ __device__ __forceinline__ void value_ring_tile(Smem& sm, int slot, int pb_i,
             cb + to[mb & 1][kt][1] + ofs));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  constexpr int kSteps = 16, kPF = 4;
+  constexpr int kSteps = 2 * KMB, kPF = 4;
   bf16x8 abuf[kPF];
 #pragma unroll
   for (int st = 0; st < kPF; ++st) abuf[st] = read_a(st);
@@ -521,54 +526,243 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
   }
 }
 
+
+// Eight-wave layout (64 query rows): loader wave LW streams ring blocks LW, LW + 2, ... of
+// every tile exactly as the value waves of the four-wave layout do (two tiles ahead, two
+// register buffers), and does nothing else; the same slots, turns and barriers as every
+// other wave.
+template <int LW>
+__device__ __forceinline__ void loader_wave(Smem& sm, const Work& w, int lane) {
+  const int n = w.n_tiles;
+  Stage<kLoads> stg[2];
+  uint32_t (&plan)[kLoads / 2][64] = sm.plan[LW];
+  make_plan(plan, lane, LW);
+  int reruns = 0;
+  while (true) {
+    const int last = max(n - 1, 0);
+    load_stage(stg[0], plan, w, 0, lane);
+    load_stage(stg[1], plan, w, min(1, last), lane);
+    store_stage(sm, stg[0], lane, 0, LW, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(stg[0], plan, w, min(2, last), lane);
+    __syncthreads();
+    store_stage(sm, stg[1], lane, 1, LW, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(stg[1], plan, w, min(3, last), lane);
+    __syncthreads();
+    store_stage(sm, stg[0], lane, 2, LW, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(stg[0], plan, w, min(4, last), lane);
+    __syncthreads();
+    if (n == 0) {
+      __syncthreads();
+      return;
+    }
+    long long seen;
+    bool restarted = false;
+    auto lslot = [&](auto par, int s) {
+      constexpr int X = decltype(par)::value;
+      seen = sm.flag[s & 1];
+      store_stage(sm, stg[X], lane, s + 1, LW, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(stg[X], plan, w, min(s + 3, last), lane);
+      restarted |= seen == rerun_tag(reruns, s - 2);
+      __syncthreads();
+    };
+    seen = sm.flag[0];
+    store_stage(sm, stg[1], lane, 3, LW, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(stg[1], plan, w, min(5, last), lane);
+    restarted = seen == rerun_tag(reruns, 0);
+    __syncthreads();
+    lslot(std::integral_constant<int, 0>(), 3);
+    if (!restarted && n + 1 > 3) {
+      for (int s = 4;; s += 2) {
+        lslot(std::integral_constant<int, 1>(), s);
+        lslot(std::integral_constant<int, 0>(), s + 1);
+        if (restarted || s + 1 >= n + 1) break;
+      }
+    }
+    if (restarted) {
+      ++reruns;
+      continue;
+    }
+    __syncthreads();
+    return;
+  }
+}
+
+// Eight-wave layout: value wave VW (0..3) owns latent columns [128 VW, 128 VW + 128) of the
+// 64 rows (128 accumulator registers); slot s multiplies tile s-2.
+template <int VW>
+__device__ __forceinline__ void value_wave128(Smem& sm, const Work& w, int lane) {
+  constexpr int NQ = 2, KMB = 4;
+  const int n32 = lane & 31, g = lane >> 5;
+  constexpr int lat0 = VW * 128;
+  const int q16 = lane >> 4, L = lane & 15;
+  const int m_base = 16 * (q16 & 1), g16 = q16 >> 1;
+  int trofs[2][2][2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int h4 = 0; h4 < 2; ++h4) {
+        const int col = lat0 + 32 * par + m_base + 4 * (L & 3);
+        const int tok = 16 * kt + 8 * g16 + 4 * h4 + (L >> 2);
+        trofs[par][kt][h4] = tok * kRowB + (((col >> 3) ^ rswz(tok)) * 16) + (col & 7) * 2;
+      }
+  const int n = w.n_tiles;
+  int reruns = 0;
+  while (true) {
+    __syncthreads();
+    __syncthreads();
+    __syncthreads();
+    if (n == 0) {
+      __syncthreads();
+      float* orow0 = w.o_part + (w.qrow0 * w.S + w.u) * kDC + lat0 + 4 * g;
+      for (int nb = 0; nb < NQ; ++nb)
+        for (int c = 0; c < 128; c += 8)
+          *reinterpret_cast<float4*>(orow0 + (32 * nb + n32) * w.S * kDC + c) =
+              make_float4(0.f, 0.f, 0.f, 0.f);
+      return;
+    }
+    f32x16 acc[KMB][NQ];
+    long long seen;
+    bool restarted = false;
+    auto vslot = [&](int s) {
+      seen = sm.flag[s & 1];
+      if (s - 2 < n)
+        value_ring_tile<NQ, false, KMB>(sm, (s - 2) & (kNB - 1), (s - 2) & 1, trofs, n32, g,
+                                        acc);
+      restarted |= seen == rerun_tag(reruns, s - 2);
+      __syncthreads();
+    };
+    seen = sm.flag[0];
+    value_ring_tile<NQ, true, KMB>(sm, 0, 0, trofs, n32, g, acc);
+    restarted = seen == rerun_tag(reruns, 0);
+    __syncthreads();
+    vslot(3);
+    if (!restarted && n + 1 > 3) {
+      for (int s = 4;; s += 2) {
+        vslot(s);
+        vslot(s + 1);
+        if (restarted || s + 1 >= n + 1) break;
+      }
+    }
+    if (restarted) {
+      ++reruns;
+      continue;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < NQ; ++nb) {
+      const float l = sm.lfin[32 * nb + n32];
+      const float inv = (l > 0.f) ? 1.f / l : 0.f;
+      float* orow = w.o_part + ((w.qrow0 + 32 * nb + n32) * w.S + w.u) * kDC + lat0 + 4 * g;
+#pragma unroll
+      for (int mb = 0; mb < KMB; ++mb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          __builtin_amdgcn_sched_barrier(0);
+          float4 v;
+          v.x = acc[mb][nb][4 * a + 0] * inv;
+          v.y = acc[mb][nb][4 * a + 1] * inv;
+          v.z = acc[mb][nb][4 * a + 2] * inv;
+          v.w = acc[mb][nb][4 * a + 3] * inv;
+          *reinterpret_cast<float4*>(orow + 32 * mb + 8 * a) = v;
+        }
+    }
+    return;
+  }
+}
+
 }  // namespace ring
 
-// One workgroup per CU (the ring takes 158 KB of LDS), so the scheduler may use the
-// whole register file of each SIMD for operand prefetch.
-template <int NQ>
-__global__ __launch_bounds__(64 * (NQ + 2), 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void decode_absorbed_mfma_ring_kernel(
+// Workgroup -> (sequence, chunk, row block): the row blocks of one (b, u) are 8 workgroups
+// apart, so they run on the same XCD; the grid's padding workgroups return (uniform for the
+// whole workgroup, before any barrier).  Expanded inside each kernel: filled through a
+// helper, the page-table reads lose their scalar (s_load) form, and a vector read of a page
+// entry waits, through the in-order load counter, for every tile load in flight.
+#define MLA_SETUP_WORK(NQ)                                                           \
+  Work w;                                                                          \
+  {                                                                                \
+    const int wg = blockIdx.x;                                                     \
+    const int rest = wg >> 3;                                                      \
+    const int y = rest % n_yblk;                                                   \
+    const int unit = (rest / n_yblk) * 8 + (wg & 7);                               \
+    if (unit >= n_units) return;                                                   \
+    const int b = unit / S;                                                        \
+    w.u = unit - b * S;                                                            \
+    w.T = lens[b];                                                                 \
+    split_range(w.T, w.u, S, kPage, split_tokens, w.lo, w.hi);                     \
+    w.n_tiles = (w.hi > w.lo) ? (w.hi - w.lo + kTT - 1) / kTT : 0;                 \
+    w.q_abs = q_abs;                                                               \
+    w.pool = pool;                                                                 \
+    w.ptb = pt + static_cast<size_t>(b) * max_pages;                               \
+    w.o_part = o_part;                                                             \
+    w.lse_part = lse_part;                                                         \
+    w.qrow0 = static_cast<size_t>(b) * s_q * H + static_cast<size_t>(y) * 32 * (NQ); \
+    w.s_q = s_q;                                                                   \
+    w.H = H;                                                                       \
+    w.y = y;                                                                       \
+    w.S = S;                                                                       \
+    w.zscale = zscale;                                                             \
+    w.slack = slack;                                                               \
+  }
+
+// 32 query rows per workgroup, one wave per SIMD (the ring takes 158 KB of LDS), so the
+// scheduler may use the whole register file of each SIMD for operand prefetch: wave 0
+// scores, waves 1 and 2 stream the chunk and multiply.
+__global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_absorbed_mfma_r32_kernel(
     const bf16_t* __restrict__ q_abs, const bf16_t* __restrict__ pool,
     const int32_t* __restrict__ pt, const int32_t* __restrict__ lens,
     float* __restrict__ o_part, float* __restrict__ lse_part, int s_q, int H, int max_pages,
     int S, int split_tokens, float zscale, float slack, int n_units, int n_yblk) {
+  constexpr int NQ = 1;
   __shared__ __attribute__((aligned(16))) ring::Smem sm;
-  const int wg = blockIdx.x;
-  const int rest = wg >> 3;
-  const int y = rest % n_yblk;
-  const int unit = (rest / n_yblk) * 8 + (wg & 7);
-  if (unit >= n_units) return;  // uniform for the whole workgroup, before any barrier
-  Work w;
-  const int b = unit / S;
-  w.u = unit - b * S;
-  w.T = lens[b];
-  split_range(w.T, w.u, S, kPage, split_tokens, w.lo, w.hi);
-  w.n_tiles = (w.hi > w.lo) ? (w.hi - w.lo + kTT - 1) / kTT : 0;
-  w.q_abs = q_abs;
-  w.pool = pool;
-  w.ptb = pt + static_cast<size_t>(b) * max_pages;
-  w.o_part = o_part;
-  w.lse_part = lse_part;
-  w.qrow0 = static_cast<size_t>(b) * s_q * H + static_cast<size_t>(y) * 32 * NQ;
-  w.s_q = s_q;
-  w.H = H;
-  w.y = y;
-  w.S = S;
-  w.zscale = zscale;
-  w.slack = slack;
+  MLA_SETUP_WORK(NQ)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (threadIdx.x == 0) sm.flag[0] = sm.flag[1] = -1;
   __syncthreads();
-  // waves 0 .. NQ-1 score (32 query rows each), waves NQ and NQ+1 value
   if (wave == 0)
     ring::score_wave<NQ, 0>(sm, w, lane);
-  else if (NQ == 2 && wave == 1)
-    ring::score_wave<NQ, (NQ == 2 ? 1 : 0)>(sm, w, lane);
-  else if (wave == NQ)
+  else if (wave == 1)
     ring::value_wave<NQ, 0>(sm, w, lane);
   else
     ring::value_wave<NQ, 1>(sm, w, lane);
 }
+
+// 64 query rows per workgroup, eight waves, two per SIMD (wave w runs on SIMD w % 4):
+// score waves 0 and 1 share SIMDs 0 and 1 with loader waves 4 and 5; value waves 2, 6 and
+// 3, 7 pair up on SIMDs 2 and 3 (36 and 32 MFMAs per SIMD per slot).  Every wave fits in
+// 256 registers; the score waves prefetch 4 operand reads (the second wave on the SIMD
+// covers what a deeper prefetch would).
+__global__ __launch_bounds__(512, 1) void decode_absorbed_mfma_r64_kernel(
+    const bf16_t* __restrict__ q_abs, const bf16_t* __restrict__ pool,
+    const int32_t* __restrict__ pt, const int32_t* __restrict__ lens,
+    float* __restrict__ o_part, float* __restrict__ lse_part, int s_q, int H, int max_pages,
+    int S, int split_tokens, float zscale, float slack, int n_units, int n_yblk) {
+  constexpr int NQ = 2;
+  __shared__ __attribute__((aligned(16))) ring::Smem sm;
+  MLA_SETUP_WORK(NQ)
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) sm.flag[0] = sm.flag[1] = -1;
+  __syncthreads();
+  switch (wave) {
+    case 0: ring::score_wave<NQ, 0, 4>(sm, w, lane); break;
+    case 1: ring::score_wave<NQ, 1, 4>(sm, w, lane); break;
+    case 2: ring::value_wave128<0>(sm, w, lane); break;
+    case 3: ring::value_wave128<1>(sm, w, lane); break;
+    case 4: ring::loader_wave<0>(sm, w, lane); break;
+    case 5: ring::loader_wave<1>(sm, w, lane); break;
+    case 6: ring::value_wave128<2>(sm, w, lane); break;
+    default: ring::value_wave128<3>(sm, w, lane); break;
+  }
+}
+
+#undef MLA_SETUP_WORK
 
 }  // namespace
 
@@ -595,12 +789,12 @@ hipError_t launch_decode_absorbed_mfma(const mla_shape_t& s, const void* q_abs,
     if (v >= 0.f && v <= 64.f) slack = v;
   }
   if (nq == 2)
-    hipLaunchKernelGGL(decode_absorbed_mfma_ring_kernel<2>, dim3(grid), dim3(256), 0, st,
+    hipLaunchKernelGGL(decode_absorbed_mfma_r64_kernel, dim3(grid), dim3(512), 0, st,
                        static_cast<const bf16_t*>(q_abs), static_cast<const bf16_t*>(pool), pt,
                        lens, o_part, lse_part, s.s_q, s.n_heads, s.max_pages, s.n_splits,
                        s.split_tokens, zscale, slack, n_units, n_yblk);
   else
-    hipLaunchKernelGGL(decode_absorbed_mfma_ring_kernel<1>, dim3(grid), dim3(192), 0, st,
+    hipLaunchKernelGGL(decode_absorbed_mfma_r32_kernel, dim3(grid), dim3(192), 0, st,
                        static_cast<const bf16_t*>(q_abs), static_cast<const bf16_t*>(pool), pt,
                        lens, o_part, lse_part, s.s_q, s.n_heads, s.max_pages, s.n_splits,
                        s.split_tokens, zscale, slack, n_units, n_yblk);
