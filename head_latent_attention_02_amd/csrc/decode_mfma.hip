@@ -405,8 +405,9 @@ __device__ __forceinline__ void value_ring_tile(Smem& sm, int slot, int pb_i,
   }
 }
 
-// Value wave VW: latent columns [256 VW, 256 VW + 256) for all 64 rows.  Slot k: its
-// share of tile k+2's loads, then the value product of tile k-1.
+// Value wave VW of the 32-row layout: latent columns [256 VW, 256 VW + 256) of the block's
+// rows (32 NQ).  It also streams half of every tile through the ring (below) and, in slot s,
+// multiplies tile s-2.
 template <int NQ, int VW>
 __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
   const int n32 = lane & 31, g = lane >> 5;
@@ -528,7 +529,7 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
 
 
 // Eight-wave layout (64 query rows): loader wave LW streams ring blocks LW, LW + 2, ... of
-// every tile exactly as the value waves of the four-wave layout do (two tiles ahead, two
+// every tile exactly as the value waves of the 32-row layout do (two tiles ahead, two
 // register buffers), and does nothing else; the same slots, turns and barriers as every
 // other wave.
 template <int LW>
