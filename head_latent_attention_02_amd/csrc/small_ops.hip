@@ -20,6 +20,9 @@ namespace {
 
 constexpr int kQB = 8;  // queries per block in a4, and in a1 above 4 queries
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
 // 8 consecutive elements: a raw chunk (one 16-byte load for bf16, two for fp32) and its
 // conversion to floats.  Kernels issue a batch of raw loads first and convert afterwards,
 // so that a whole batch is in flight at once.
@@ -160,6 +163,108 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
   }
   if (blockIdx.y == 0) {
     for (int idx = tid; idx < nq * d_r; idx += blockDim.x) {
+      const int jq = idx / d_r, r = idx - jq * d_r;
+      const size_t qrow = static_cast<size_t>(q0 + jq) * H + h;
+      q_abs[qrow * D + d_c + r] = q[qrow * dq + d_n + r];
+    }
+  }
+}
+
+// a1 on the matrix cores (bf16, d_n = 128, 16 or more queries).  Block (head h, 128 latent
+// columns c0 .., 32 NB queries q0 ..), 4 waves; wave w computes q_abs^T[c0 + 32 w + m][q] =
+// sum_i W_UK[h][i][c] q[q][i] with v_mfma_f32_32x32x16_bf16: the weight slice, staged once in
+// LDS (rows of 256 bytes, 16-byte chunks XOR-swizzled by row), is the A operand, read
+// transposed with ds_read_b64_tr_b16; the queries' no-position parts are the B operand,
+// 16-byte loads in their natural layout.  Each weight byte is read once per 32 NB queries
+// (once per 8 in absorb_q_kernel), which is what the multi-query decode steps need.
+constexpr int kAmC = 128;   // latent columns per block
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+__device__ __forceinline__ int am_swz(int i) { return (((i >> 1) & 1) << 2) | ((i >> 2) & 3); }
+
+template <int NB>
+__global__ __launch_bounds__(256) void absorb_q_mfma_kernel(const bf16_t* __restrict__ q,
+                                                            const bf16_t* __restrict__ w_uk,
+                                                            bf16_t* __restrict__ q_abs, int NQ,
+                                                            int H, int Hw, int d_r, int d_c) {
+  constexpr int d_n = 128;
+  __shared__ __align__(16) char ws[d_n * kAmC * 2];
+  const int h = blockIdx.x, c0 = blockIdx.y * kAmC, q0 = blockIdx.z * 32 * NB;
+  const int wh = h / (H / Hw);
+  const int dq = d_n + d_r, D = d_c + d_r;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n32 = lane & 31, g = lane >> 5;
+  const int nq = min(32 * NB, NQ - q0);
+  // weight slice W_UK[wh][0:128][c0:c0+128]: 2048 chunks of 16 bytes, 8 per thread
+  const bf16_t* W = w_uk + static_cast<size_t>(wh) * d_n * d_c + c0;
+  uint4 wv[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int idx = tid + 256 * k, i = idx >> 4, ch = idx & 15;
+    wv[k] = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(i) * d_c + 8 * ch);
+  }
+  // B operands: query 32 nb + n32, rows i = 16 kt + 8 g .. +8 (zeros past the last query)
+  bf16x8_t qb[NB][8];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int qi = 32 * nb + n32;
+    const bf16_t* qp = q + (static_cast<size_t>(q0 + min(qi, nq - 1)) * H + h) * dq + 8 * g;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) {
+      const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kt);
+      qb[nb][kt] = (qi < nq) ? v : bf16x8_t{};
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int idx = tid + 256 * k, i = idx >> 4, ch = idx & 15;
+    *reinterpret_cast<uint4*>(ws + i * 256 + ((ch ^ am_swz(i)) * 16)) = wv[k];
+  }
+  __syncthreads();
+  // A operand of K-step kt for this wave's 32 columns: the lane mapping of the transposed
+  // read (4 rows x 4 columns per 16-lane group, two reads per operand)
+  const int q16 = lane >> 4, L = lane & 15;
+  const int col = 32 * (wave & 1) + 16 * (q16 & 1) + 4 * (L & 3);
+  int to[2];
+#pragma unroll
+  for (int h4 = 0; h4 < 2; ++h4) {
+    const int i = 8 * (q16 >> 1) + 4 * h4 + (L >> 2);
+    to[h4] = i * 256 + (((col >> 3) ^ am_swz(i)) * 16) + (col & 7) * 2 + 128 * (wave >> 1);
+  }
+  f32x16_t acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16_t{};
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt) {
+    // rows 16 kt .. +16 keep the swizzle of rows 0 .. 15 (it reads row bits 1-3 only)
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)(const __attribute__((address_space(3))) char*)(ws + to[0] + 4096 * kt));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)(const __attribute__((address_space(3))) char*)(ws + to[1] + 4096 * kt));
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[nb][kt], acc[nb], 0, 0, 0);
+  }
+  // lane (query n32, half g) holds columns 8 (j / 4) + 4 g + j % 4 of the wave's 32
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int qi = 32 * nb + n32;
+    if (qi >= nq) continue;
+    bf16_t* orow = q_abs + static_cast<size_t>(q0 + qi) * H * D + static_cast<size_t>(h) * D +
+                   c0 + 32 * wave + 4 * g;
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      uint32_t pk[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        pk[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[nb][4 * jg + 2 * e]))) |
+                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[nb][4 * jg + 2 * e + 1]))) << 16);
+      *reinterpret_cast<uint2*>(orow + 8 * jg) = make_uint2(pk[0], pk[1]);
+    }
+  }
+  if (blockIdx.y == 0) {
+    for (int idx = tid; idx < nq * d_r; idx += 256) {
       const int jq = idx / d_r, r = idx - jq * d_r;
       const size_t qrow = static_cast<size_t>(q0 + jq) * H + h;
       q_abs[qrow * D + d_c + r] = q[qrow * dq + d_n + r];
@@ -330,8 +435,6 @@ __global__ __launch_bounds__(256) void out_uv_kernel(const float* __restrict__ o
 // operand (query = N, padded to 32).  One block of 4 waves per (head, 32 value rows); the
 // waves split the latent dimension (at d_c = 512 each issues all its loads at once) and
 // meet in LDS; query blocks of 32 in turn.
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kUvmSteps = 8;
 constexpr int kUvmWaves = 4;
 
@@ -634,6 +737,24 @@ hipError_t launch_absorb_q(const mla_shape_t& s, const void* q, const void* w_uk
                          static_cast<bf16_t*>(q_abs), NQ, s.n_heads, s.n_wheads, s.d_nope,
                          s.d_rope, s.d_c);
   };
+  // 16 or more bf16 queries with 128-wide no-position parts: the matrix-core kernel
+  if (s.dtype == MLA_BF16 && s.d_nope == 128 && s.d_c % kAmC == 0 && NQ >= 16) {
+    auto mf = [&](auto nbc) {
+      constexpr int NB = decltype(nbc)::value;
+      dim3 grid(s.n_heads, s.d_c / kAmC, (NQ + 32 * NB - 1) / (32 * NB));
+      hipLaunchKernelGGL((absorb_q_mfma_kernel<NB>), grid, dim3(256), 0, st,
+                         static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(w_uk),
+                         static_cast<bf16_t*>(q_abs), NQ, s.n_heads, s.n_wheads, s.d_rope,
+                         s.d_c);
+    };
+    if (NQ <= 32)
+      mf(std::integral_constant<int, 1>{});
+    else if (NQ <= 64)
+      mf(std::integral_constant<int, 2>{});
+    else
+      mf(std::integral_constant<int, 4>{});
+    return hipGetLastError();
+  }
   if (NQ <= 4)
     go(std::integral_constant<int, 4>{});
   else
