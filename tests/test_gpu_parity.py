@@ -141,6 +141,26 @@ def test_bf16_step_entry_point_matches_steps(name, s_q, ctx, S):
 
 
 
+@pytest.mark.parametrize("name,batch,s_q", [
+    ("dsv2-b16-t4096", 3, 1), ("dsv2-b16-t4096", 12, 1), ("dsv2-b16-t4096", 17, 1),
+    ("dsv2-b16-t4096", 33, 1), ("dsv2-b16-t4096", 50, 2), ("dsv2-b16-t4096", 65, 2),
+    ("gqla-b32-t8192", 20, 1)])
+def test_absorb_query_counts(name, batch, s_q):
+    """a1 alone at query counts that exercise both kernels: 4- and 8-query VALU blocks (3,
+    12), and matrix-core workgroups of 1, 2 or 4 blocks of 32 queries, partly filled (17,
+    33, 100) or more than one along the queries (130), at 128 heads and at GQLA's grouped
+    heads (32 heads over 8 weight heads)."""
+    cfg = small(name, batch=batch, s_q=s_q, ctx=("list", [64 + 7 * b for b in range(batch)]))
+    inp = make_inputs(cfg, seed=21)
+    announce(f"case absorb {cfg.name} NQ={batch * s_q} H={cfg.n_heads}/{cfg.n_wheads}")
+    d = DeviceInputs(inp)
+    d.q_abs.fill_(float("nan"))
+    mla.mla_absorb_q(d.shape, d.q, d.w_uk, d.q_abs)
+    torch.cuda.synchronize()
+    want = ref.absorb_query(inp.q, inp.w_uk, cfg.d_nope)
+    assert rel_err(d.q_abs.float().cpu().numpy(), want) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("S,L,ctx", [
     (1, 0, [1000, 64]), (4, 0, [4096, 577]), (3, 128, [300, 129]), (8, 0, [33, 1])])
 def test_bf16_mla_small_all_steps(S, L, ctx):
