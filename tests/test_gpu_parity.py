@@ -456,6 +456,17 @@ def test_reference_moves_rerun_path(slack, monkeypatch):
     assert errs["out"] <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("slack", ["0", "0.25"])
+def test_reference_moves_rerun_path_32_row_blocks(slack, monkeypatch):
+    """The rerun path of the 32-row-block kernel (GQLA's absorbed shape, 32 heads): with no
+    slack every raised maximum reruns the chunk; the result must not change."""
+    monkeypatch.setenv("MLA_DECODE_REF_SLACK", slack)
+    cfg = small("gqla-b32-t8192", batch=3, s_q=1, ctx=("list", [1500, 700, 65]))
+    assert cfg.s_q * cfg.n_heads == 32          # one block of 32 query rows per sequence
+    errs = check_absorbed_all_steps(make_inputs(cfg, seed=14), S=3)
+    assert errs["out"] <= TOL["bf16"]
+
+
 def test_growing_scores_move_the_reference_by_large_steps():
     """Scores that climb by ~38 log2 units per tile move the reference at the default
     slack on every tile; the result must still match the oracle."""
