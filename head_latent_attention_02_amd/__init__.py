@@ -5,9 +5,9 @@ The compute lives in ``libmla.so`` (hand-written HIP kernels behind the C ABI of
 the library; the first call does, and raises if the library has not been built.
 """
 from ._lib import (  # noqa: F401
-    EXPORTS, LIB_PATH, MLA_BF16, MLA_ERR_HIP, MLA_ERR_NULL, MLA_ERR_SHAPE,
+    CHECKED_LIB_PATH, EXPORTS, LIB_PATH, MLA_BF16, MLA_ERR_HIP, MLA_ERR_NULL, MLA_ERR_SHAPE,
     MLA_ERR_UNSUPPORTED, MLA_F32, MLA_OK, MlaError, MlaShape, gqla_cache_scalars_per_token,
     gqla_decode_gqa, gqla_decode_kernel_kind, gqla_decode_step, gqla_expand_cache, load,
     make_shape, mla_absorb_q, mla_cache_append, mla_cache_scalars_per_token,
     mla_decode_absorbed, mla_decode_kernel_kind, mla_decode_step, mla_out_uv,
-    mla_splitkv_combine, mla_status_str)
+    mla_checked_bad_pages, mla_splitkv_combine, mla_status_str)

@@ -11,6 +11,8 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+# the same library built with MLA_CHECKED: page-table entries bounds-checked on the device
+CHECKED_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_checked.so")
 
 MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = range(5)
 MLA_F32, MLA_BF16 = 0, 1
@@ -20,7 +22,8 @@ EXPORTS = ("mla_absorb_q", "mla_decode_absorbed", "mla_splitkv_combine", "mla_ou
            "gqla_decode_gqa", "gqla_expand_cache", "mla_cache_append", "mla_decode_step",
            "gqla_decode_step",
            "mla_cache_scalars_per_token", "gqla_cache_scalars_per_token",
-           "mla_decode_kernel_kind", "gqla_decode_kernel_kind", "mla_status_str")
+           "mla_decode_kernel_kind", "gqla_decode_kernel_kind", "mla_checked_bad_pages",
+           "mla_status_str")
 
 
 class MlaShape(ctypes.Structure):
@@ -43,17 +46,18 @@ class MlaError(RuntimeError):
         super().__init__(f"{fn} failed: status {status} ({status_str(status)})")
 
 
-_lib = None
+_libs = {}
 
 
-def load():
-    """Load libmla.so (once).  Raises if it has not been built."""
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+def load(checked=False):
+    """Load libmla.so, or libmla_checked.so with checked=True (once each).  Raises if it has
+    not been built."""
+    path = CHECKED_LIB_PATH if checked else LIB_PATH
+    if path not in _libs:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
                                "`python -c 'import __graft_entry__ as g; g.build()'`")
-        lib = ctypes.CDLL(LIB_PATH)
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         S = ctypes.POINTER(MlaShape)
         sig = {
@@ -76,9 +80,16 @@ def load():
         for name in ("mla_decode_kernel_kind", "gqla_decode_kernel_kind"):
             f = getattr(lib, name)
             f.argtypes, f.restype = [S], ctypes.c_int32
+        lib.mla_checked_bad_pages.argtypes, lib.mla_checked_bad_pages.restype = [], ctypes.c_int32
         lib.mla_status_str.argtypes, lib.mla_status_str.restype = [ctypes.c_int], ctypes.c_char_p
-        _lib = lib
-    return _lib
+        _libs[path] = lib
+    return _libs[path]
+
+
+def mla_checked_bad_pages(checked=True):
+    """1 if a checked call met an out-of-range page-table entry since the last query (then
+    cleared), 0 if not; -1 from libmla.so, which has no checks; -2 on a HIP error."""
+    return int(load(checked).mla_checked_bad_pages())
 
 
 def make_shape(batch, s_q, n_heads, n_wheads, d_c, d_rope, d_nope, d_v, max_pages,

@@ -1,7 +1,9 @@
-"""Build libmla.so (HIP for gfx950) in-tree.
+"""Build libmla.so (HIP for gfx950) in-tree, and its checked variant.
 
 Every ``csrc/*.hip`` file is compiled by hipcc into ``_build/`` and linked into
-``head_latent_attention_02_amd/libmla.so``.  Packed-fp32 instruction selection is
+``head_latent_attention_02_amd/libmla.so``; the same sources compiled with ``MLA_CHECKED``
+(objects in ``_build/checked/``) make ``libmla_checked.so``, whose decode kernels
+bounds-check the page-table entries they read.  Packed-fp32 instruction selection is
 disabled for device code (``-packed-fp32-ops``); the host pass warns that it does not know
 that feature, which is harmless.
 """
@@ -17,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libmla.so")
+CHECKED_LIB_PATH = os.path.join(PKG, "libmla_checked.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -25,8 +28,8 @@ CFLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", f"-I{INCLUDE}"
           "-Wno-unused-command-line-argument"]
 
 
-def _compile(src, extra):
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(src, extra, out_dir=BUILD_DIR):
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
     cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -34,20 +37,29 @@ def _compile(src, extra):
     return obj
 
 
-def build(verbose=False, jobs=8, extra_flags=()):
-    """Compile every HIP source and link libmla.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def _build_one(lib_path, out_dir, flags, jobs, verbose):
+    os.makedirs(out_dir, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), sources))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, list(flags), out_dir), sources))
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB_PATH} from {len(sources)} sources", file=sys.stderr)
+        print(f"built {lib_path} from {len(sources)} sources", file=sys.stderr)
+    return lib_path
+
+
+def build(verbose=False, jobs=8, extra_flags=(), checked=True):
+    """Compile every HIP source and link libmla.so (and libmla_checked.so unless
+    checked=False); returns the path of libmla.so."""
+    _build_one(LIB_PATH, BUILD_DIR, extra_flags, jobs, verbose)
+    if checked:
+        _build_one(CHECKED_LIB_PATH, os.path.join(BUILD_DIR, "checked"),
+                   [*extra_flags, "-DMLA_CHECKED"], jobs, verbose)
     return LIB_PATH
 
 

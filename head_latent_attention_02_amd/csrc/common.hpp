@@ -12,6 +12,25 @@ typedef uint16_t bf16_t;  // bf16 storage: the upper half of an IEEE binary32
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Checked builds (compiled with MLA_CHECKED) bounds-check every device-resident page-table
+// entry before it is used as an address: an entry outside [0, num_pages) is replaced by page
+// 0, so nothing outside the pool is read, and sets the library's bad-page flag (*bad = 1),
+// which mla_checked_bad_pages reports.  Unchecked builds compile the check out.
+#ifdef MLA_CHECKED
+constexpr bool kChecked = true;
+#else
+constexpr bool kChecked = false;
+#endif
+__device__ __forceinline__ int checked_page(int page, int num_pages, unsigned int* bad) {
+  if constexpr (kChecked) {
+    if (page < 0 || page >= num_pages) {
+      if (bad) *bad = 1u;
+      return 0;
+    }
+  }
+  return page;
+}
+
 __device__ __forceinline__ float ldf(const float* p) { return *p; }
 __device__ __forceinline__ float ldf(const bf16_t* p) {
   return __uint_as_float(static_cast<uint32_t>(*p) << 16);

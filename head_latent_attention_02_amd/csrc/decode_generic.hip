@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void decode_absorbed_generic_kernel(
     const E* __restrict__ q_abs, const E* __restrict__ pool, const int32_t* __restrict__ pt,
     const int32_t* __restrict__ lens, float* __restrict__ o_part,
     float* __restrict__ lse_part, int s_q, int H, int d_c, int D, int P, int max_pages,
-    int S, int split_tokens, float scale) {
+    int S, int split_tokens, float scale, int num_pages, unsigned int* bad) {
   const int u = blockIdx.x, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.y * 4 + (threadIdx.x >> 6);  // row = s * H + h
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void decode_absorbed_generic_kernel(
   }
   float m = -INFINITY, l = 0.f;
   for (int t = lo; t < top; ++t) {
-    const int page = pt[static_cast<size_t>(b) * max_pages + t / P];
+    const int page = checked_page(pt[static_cast<size_t>(b) * max_pages + t / P], num_pages, bad);
     const E* rp = pool + (static_cast<size_t>(page) * P + (t % P)) * D;
     float x[kMaxChunks];
     float part = 0.f;
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void gqa_decode_generic_kernel(
     const E* __restrict__ krp, const int32_t* __restrict__ pt,
     const int32_t* __restrict__ lens, float* __restrict__ o_part,
     float* __restrict__ lse_part, int s_q, int H, int G, int d_n, int d_r, int d_v, int P,
-    int max_pages, int S, int split_tokens, float scale) {
+    int max_pages, int S, int split_tokens, float scale, int num_pages, unsigned int* bad) {
   const int u = blockIdx.x, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void gqa_decode_generic_kernel(
   }
   float m = -INFINITY, l = 0.f;
   for (int t = lo; t < top; ++t) {
-    const int page = pt[static_cast<size_t>(b) * max_pages + t / P];
+    const int page = checked_page(pt[static_cast<size_t>(b) * max_pages + t / P], num_pages, bad);
     const size_t slot = static_cast<size_t>(page) * P + (t % P);
     const E* krow = kp + (slot * G + j) * d_n;
     const E* rrow = krp + slot * d_r;
@@ -147,26 +147,28 @@ __global__ __launch_bounds__(256) void gqa_decode_generic_kernel(
 hipError_t launch_decode_absorbed_generic(const mla_shape_t& s, const void* q_abs,
                                           const void* pool, const int32_t* pt,
                                           const int32_t* lens, float* o_part,
-                                          float* lse_part, hipStream_t st) {
+                                          float* lse_part, unsigned int* bad, hipStream_t st) {
   const int D = s.d_c + s.d_rope;
   dim3 grid(s.n_splits, (s.s_q * s.n_heads + 3) / 4, s.batch);
   if (s.dtype == MLA_F32)
     hipLaunchKernelGGL(decode_absorbed_generic_kernel<float>, grid, dim3(256), 0, st,
                        static_cast<const float*>(q_abs), static_cast<const float*>(pool), pt,
                        lens, o_part, lse_part, s.s_q, s.n_heads, s.d_c, D, s.page_size,
-                       s.max_pages, s.n_splits, s.split_tokens, s.softmax_scale);
+                       s.max_pages, s.n_splits, s.split_tokens, s.softmax_scale,
+                       s.num_pages, bad);
   else
     hipLaunchKernelGGL(decode_absorbed_generic_kernel<bf16_t>, grid, dim3(256), 0, st,
                        static_cast<const bf16_t*>(q_abs), static_cast<const bf16_t*>(pool),
                        pt, lens, o_part, lse_part, s.s_q, s.n_heads, s.d_c, D, s.page_size,
-                       s.max_pages, s.n_splits, s.split_tokens, s.softmax_scale);
+                       s.max_pages, s.n_splits, s.split_tokens, s.softmax_scale,
+                       s.num_pages, bad);
   return hipGetLastError();
 }
 
 hipError_t launch_gqa_decode_generic(const mla_shape_t& s, const void* q, const void* k,
                                      const void* v, const void* kr, const int32_t* pt,
                                      const int32_t* lens, float* o_part, float* lse_part,
-                                     hipStream_t st) {
+                                     unsigned int* bad, hipStream_t st) {
   dim3 grid(s.n_splits, (s.s_q * s.n_heads + 3) / 4, s.batch);
   if (s.dtype == MLA_F32)
     hipLaunchKernelGGL(gqa_decode_generic_kernel<float>, grid, dim3(256), 0, st,
@@ -174,14 +176,14 @@ hipError_t launch_gqa_decode_generic(const mla_shape_t& s, const void* q, const 
                        static_cast<const float*>(v), static_cast<const float*>(kr), pt, lens,
                        o_part, lse_part, s.s_q, s.n_heads, s.n_wheads, s.d_nope, s.d_rope,
                        s.d_v, s.page_size, s.max_pages, s.n_splits, s.split_tokens,
-                       s.softmax_scale);
+                       s.softmax_scale, s.num_pages, bad);
   else
     hipLaunchKernelGGL(gqa_decode_generic_kernel<bf16_t>, grid, dim3(256), 0, st,
                        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                        static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(kr), pt,
                        lens, o_part, lse_part, s.s_q, s.n_heads, s.n_wheads, s.d_nope,
                        s.d_rope, s.d_v, s.page_size, s.max_pages, s.n_splits,
-                       s.split_tokens, s.softmax_scale);
+                       s.split_tokens, s.softmax_scale, s.num_pages, bad);
   return hipGetLastError();
 }
 

@@ -67,6 +67,8 @@ struct Work {
   int lo, hi, n_tiles, T, s_q, H, y, S, u;
   float zscale;
   float slack;          // lazy-reference slack (log2 units)
+  int num_pages;        // pool bound, for checked builds
+  unsigned int* bad;    // bad-page flag, for checked builds
 };
 
 namespace ring {
@@ -145,7 +147,7 @@ __device__ __forceinline__ void load_stage(Stage<kLoads>& st,
   const int valid = __builtin_amdgcn_readfirstlane(max(min(w.hi - t0, kTT), 0));
   // an empty chunk (valid == 0) reads nothing, not even its page-table entry
   int page = 0;
-  if (valid > 0) page = w.ptb[t0 >> 6];
+  if (valid > 0) page = checked_page(w.ptb[t0 >> 6], w.num_pages, w.bad);
   const bf16_t* base = w.pool + (static_cast<size_t>(page) * kPage + (t0 & (kPage - 1))) * kD;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16_t*>(base), 0, valid * kRowB, kBufWord3);
@@ -710,6 +712,8 @@ __device__ __forceinline__ void value_wave128(Smem& sm, const Work& w, int lane)
     w.S = S;                                                                       \
     w.zscale = zscale;                                                             \
     w.slack = slack;                                                               \
+    w.num_pages = num_pages;                                                       \
+    w.bad = bad;                                                                   \
   }
 
 // 32 query rows per workgroup, one wave per SIMD (the ring takes 158 KB of LDS), so the
@@ -720,7 +724,8 @@ void decode_absorbed_mfma_r32_kernel(
     const bf16_t* __restrict__ q_abs, const bf16_t* __restrict__ pool,
     const int32_t* __restrict__ pt, const int32_t* __restrict__ lens,
     float* __restrict__ o_part, float* __restrict__ lse_part, int s_q, int H, int max_pages,
-    int S, int split_tokens, float zscale, float slack, int n_units, int n_yblk) {
+    int S, int split_tokens, float zscale, float slack, int n_units, int n_yblk,
+    int num_pages, unsigned int* bad) {
   constexpr int NQ = 1;
   __shared__ __attribute__((aligned(16))) ring::Smem sm;
   MLA_SETUP_WORK(NQ)
@@ -744,7 +749,8 @@ __global__ __launch_bounds__(512, 1) void decode_absorbed_mfma_r64_kernel(
     const bf16_t* __restrict__ q_abs, const bf16_t* __restrict__ pool,
     const int32_t* __restrict__ pt, const int32_t* __restrict__ lens,
     float* __restrict__ o_part, float* __restrict__ lse_part, int s_q, int H, int max_pages,
-    int S, int split_tokens, float zscale, float slack, int n_units, int n_yblk) {
+    int S, int split_tokens, float zscale, float slack, int n_units, int n_yblk,
+    int num_pages, unsigned int* bad) {
   constexpr int NQ = 2;
   __shared__ __attribute__((aligned(16))) ring::Smem sm;
   MLA_SETUP_WORK(NQ)
@@ -775,7 +781,7 @@ bool decode_absorbed_mfma_supported(const mla_shape_t& s) {
 hipError_t launch_decode_absorbed_mfma(const mla_shape_t& s, const void* q_abs,
                                        const void* pool, const int32_t* pt,
                                        const int32_t* lens, float* o_part, float* lse_part,
-                                       hipStream_t st) {
+                                       unsigned int* bad, hipStream_t st) {
   const int rows = s.s_q * s.n_heads;
   const int nq = (rows % 64 == 0) ? 2 : 1;
   const int n_yblk = rows / (32 * nq);
@@ -793,12 +799,12 @@ hipError_t launch_decode_absorbed_mfma(const mla_shape_t& s, const void* q_abs,
     hipLaunchKernelGGL(decode_absorbed_mfma_r64_kernel, dim3(grid), dim3(512), 0, st,
                        static_cast<const bf16_t*>(q_abs), static_cast<const bf16_t*>(pool), pt,
                        lens, o_part, lse_part, s.s_q, s.n_heads, s.max_pages, s.n_splits,
-                       s.split_tokens, zscale, slack, n_units, n_yblk);
+                       s.split_tokens, zscale, slack, n_units, n_yblk, s.num_pages, bad);
   else
     hipLaunchKernelGGL(decode_absorbed_mfma_r32_kernel, dim3(grid), dim3(192), 0, st,
                        static_cast<const bf16_t*>(q_abs), static_cast<const bf16_t*>(pool), pt,
                        lens, o_part, lse_part, s.s_q, s.n_heads, s.max_pages, s.n_splits,
-                       s.split_tokens, zscale, slack, n_units, n_yblk);
+                       s.split_tokens, zscale, slack, n_units, n_yblk, s.num_pages, bad);
   return hipGetLastError();
 }
 

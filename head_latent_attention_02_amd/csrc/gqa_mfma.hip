@@ -76,6 +76,8 @@ struct Args {
   const bf16_t* kr;
   const int32_t* ptb;   // page-table row of sequence b
   int G, j, lo, hi;
+  int num_pages;        // pool bound, for checked builds
+  unsigned int* bad;    // bad-page flag, for checked builds
 };
 
 struct Red {
@@ -101,7 +103,7 @@ __device__ __forceinline__ u32x4 ld_stream(const bf16_t* p) {
 }
 
 __device__ __forceinline__ void load_tile(Tile& tl, const Args& a, int t0, int lane) {
-  const int page = a.ptb[t0 >> 6];
+  const int page = checked_page(a.ptb[t0 >> 6], a.num_pages, a.bad);
   const size_t slot0 = static_cast<size_t>(page) * kPage + (t0 & (kPage - 1));
   const int valid = a.hi - t0;
 #pragma unroll
@@ -220,7 +222,8 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_mfma_kernel(
     const bf16_t* __restrict__ vpool, const bf16_t* __restrict__ krpool,
     const int32_t* __restrict__ pt, const int32_t* __restrict__ lens,
     float* __restrict__ o_part, float* __restrict__ lse_part, int s_q, int H, int G,
-    int max_pages, int S, int split_tokens, float zscale, int n_units) {
+    int max_pages, int S, int split_tokens, float zscale, int n_units, int num_pages,
+    unsigned int* bad) {
   __shared__ __attribute__((aligned(16))) Smem sm;
   const int wg = blockIdx.x;
   const int rest = wg >> 3;
@@ -234,6 +237,8 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_mfma_kernel(
   a.v = vpool;
   a.kr = krpool;
   a.ptb = pt + static_cast<size_t>(b) * max_pages;
+  a.num_pages = num_pages;
+  a.bad = bad;
   a.G = G;
   a.j = j;
   split_range(T, u, S, kPage, split_tokens, a.lo, a.hi);
@@ -334,14 +339,15 @@ bool gqa_decode_mfma_supported(const mla_shape_t& s) {
 hipError_t launch_gqa_decode_mfma(const mla_shape_t& s, const void* q, const void* k,
                                   const void* v, const void* kr, const int32_t* pt,
                                   const int32_t* lens, float* o_part, float* lse_part,
-                                  hipStream_t st) {
+                                  unsigned int* bad, hipStream_t st) {
   const int n_units = s.batch * s.n_splits;
   const unsigned grid = static_cast<unsigned>((n_units + 7) / 8) * 8u * s.n_wheads;
   hipLaunchKernelGGL(gqa_decode_mfma_kernel, dim3(grid), dim3(256), 0, st,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                      static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(kr), pt, lens,
                      o_part, lse_part, s.s_q, s.n_heads, s.n_wheads, s.max_pages,
-                     s.n_splits, s.split_tokens, s.softmax_scale * kLog2e, n_units);
+                     s.n_splits, s.split_tokens, s.softmax_scale * kLog2e, n_units,
+                     s.num_pages, bad);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 // Host-side launchers of the kernels (one translation unit per kernel family).
-// Every launcher assumes its shape has been validated by the C-ABI layer.
+// Every launcher assumes its shape has been validated by the C-ABI layer.  `bad` is the
+// bad-page flag of checked builds (nullptr, and unused, in unchecked ones).
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -12,11 +13,11 @@ hipError_t launch_absorb_q(const mla_shape_t& s, const void* q, const void* w_uk
 hipError_t launch_decode_absorbed_generic(const mla_shape_t& s, const void* q_abs,
                                           const void* pool, const int32_t* pt,
                                           const int32_t* lens, float* o_part,
-                                          float* lse_part, hipStream_t st);
+                                          float* lse_part, unsigned int* bad, hipStream_t st);
 hipError_t launch_decode_absorbed_mfma(const mla_shape_t& s, const void* q_abs,
                                        const void* pool, const int32_t* pt,
                                        const int32_t* lens, float* o_part, float* lse_part,
-                                       hipStream_t st);
+                                       unsigned int* bad, hipStream_t st);
 bool decode_absorbed_mfma_supported(const mla_shape_t& s);
 hipError_t launch_combine(const mla_shape_t& s, int width, const float* o_part,
                           const float* lse_part, float* o, float* lse, hipStream_t st);
@@ -31,11 +32,11 @@ hipError_t launch_out_uv(const mla_shape_t& s, const float* o_lat, const void* w
 hipError_t launch_gqa_decode_generic(const mla_shape_t& s, const void* q, const void* k,
                                      const void* v, const void* kr, const int32_t* pt,
                                      const int32_t* lens, float* o_part, float* lse_part,
-                                     hipStream_t st);
+                                     unsigned int* bad, hipStream_t st);
 hipError_t launch_gqa_decode_mfma(const mla_shape_t& s, const void* q, const void* k,
                                   const void* v, const void* kr, const int32_t* pt,
                                   const int32_t* lens, float* o_part, float* lse_part,
-                                  hipStream_t st);
+                                  unsigned int* bad, hipStream_t st);
 bool gqa_decode_mfma_supported(const mla_shape_t& s);
 hipError_t launch_cache_append(const mla_shape_t& s, int d_model, float rope_base,
                                const void* h, const void* w_dkv, const void* w_kr,

@@ -3,10 +3,23 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "common.hpp"
 #include "launch.hpp"
 #include "mla.h"
 
 namespace {
+
+// The bad-page flag of checked builds (see checked_page): one word per device, set by the
+// decode kernels, read and cleared by mla_checked_bad_pages.
+__device__ unsigned int g_bad_pages;
+
+// This device's flag for the kernels (checked builds), nullptr if it cannot be found.
+unsigned int* bad_page_flag() {
+  if (!mla::kChecked) return nullptr;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_bad_pages)) != hipSuccess) return nullptr;
+  return static_cast<unsigned int*>(p);
+}
 
 constexpr int kMaxDim = 1024;
 
@@ -92,11 +105,15 @@ mla_status_t mla_decode_absorbed(const mla_shape_t* s, const void* q_abs, const 
   if (v != MLA_OK) return v;
   if (!q_abs || !kv_pool || !page_table || !ctx_lens || !o_part || !lse_part)
     return MLA_ERR_NULL;
+  unsigned int* bad = bad_page_flag();
+  if (mla::kChecked && !bad) return MLA_ERR_HIP;
   if (mla::decode_absorbed_mfma_supported(*s))
     return hip_status(mla::launch_decode_absorbed_mfma(*s, q_abs, kv_pool, page_table,
-                                                       ctx_lens, o_part, lse_part, stream));
+                                                       ctx_lens, o_part, lse_part, bad,
+                                                       stream));
   return hip_status(mla::launch_decode_absorbed_generic(*s, q_abs, kv_pool, page_table,
-                                                        ctx_lens, o_part, lse_part, stream));
+                                                        ctx_lens, o_part, lse_part, bad,
+                                                        stream));
 }
 
 mla_status_t mla_splitkv_combine(const mla_shape_t* s, int32_t width, const float* o_part,
@@ -127,11 +144,13 @@ mla_status_t gqla_decode_gqa(const mla_shape_t* s, const void* q, const void* k_
   if (!q || !k_pool || !v_pool || !page_table || !ctx_lens || !o_part || !lse_part)
     return MLA_ERR_NULL;
   if (s->d_rope > 0 && !kr_pool) return MLA_ERR_NULL;
+  unsigned int* bad = bad_page_flag();
+  if (mla::kChecked && !bad) return MLA_ERR_HIP;
   if (mla::gqa_decode_mfma_supported(*s))
     return hip_status(mla::launch_gqa_decode_mfma(*s, q, k_pool, v_pool, kr_pool, page_table,
-                                                  ctx_lens, o_part, lse_part, stream));
+                                                  ctx_lens, o_part, lse_part, bad, stream));
   return hip_status(mla::launch_gqa_decode_generic(*s, q, k_pool, v_pool, kr_pool, page_table,
-                                                   ctx_lens, o_part, lse_part, stream));
+                                                   ctx_lens, o_part, lse_part, bad, stream));
 }
 
 mla_status_t gqla_expand_cache(const mla_shape_t* s, const void* kv_pool, const void* w_uk,
@@ -196,3 +215,16 @@ mla_status_t gqla_decode_step(const mla_shape_t* s, const void* q, const void* k
 }
 
 }  // extern "C"
+
+int32_t mla_checked_bad_pages(void) {
+  if (!mla::kChecked) return -1;
+  unsigned int v = 0;
+  const unsigned int zero = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_bad_pages), sizeof(v), 0, hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return -2;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(g_bad_pages), &zero, sizeof(zero), 0,
+                        hipMemcpyHostToDevice) != hipSuccess)
+    return -2;
+  return v ? 1 : 0;
+}

@@ -26,8 +26,10 @@
  *    ones; query row s (0 <= s < s_q) attends to tokens 0 .. T_b - s_q + s (causal
  *    within the new tokens).  ctx_lens and page_table are device data and must satisfy
  *    0 <= T_b <= max_pages * page_size and 0 <= page_table[b][i] < num_pages for
- *    i < ceil(T_b / page_size); entries past that are never read (use -1).  These
- *    device values are not validated: breaking them is undefined behaviour.
+ *    i < ceil(T_b / page_size); entries past that are never read (use -1).  libmla.so
+ *    does not validate these device values: breaking them is undefined behaviour.  The
+ *    checked build libmla_checked.so bounds-checks page-table entries (see
+ *    mla_checked_bad_pages).
  *  - Split-KV: sequence b is cut into n_splits chunks.  split_tokens == 0: chunk length
  *    L_b = ceil(ceil(T_b / n_splits) / page_size) * page_size; split_tokens > 0: fixed
  *    L = split_tokens (a multiple of page_size, and n_splits * L must cover
@@ -192,6 +194,16 @@ int64_t gqla_cache_scalars_per_token(const mla_shape_t* shape);
  * 0 = generic kernel, -1 = invalid or unsupported shape.  Host-only, no HIP call. */
 int32_t mla_decode_kernel_kind(const mla_shape_t* shape);
 int32_t gqla_decode_kernel_kind(const mla_shape_t* shape);
+
+/* Checked builds only.  libmla_checked.so (the same sources compiled with MLA_CHECKED)
+ * bounds-checks every page-table entry that the decode entry points (a2, a5 and the two step
+ * helpers) read on the device: an entry outside [0, num_pages) is replaced by page 0, so
+ * nothing outside the pool is read, and sets a per-device flag; the outputs of such a call
+ * are meaningless.  Returns 1 if the current device's flag was set since the last call, else
+ * 0, and clears it; -1 in libmla.so (no checks; out-of-range entries are undefined behaviour
+ * there); -2 on a HIP error.  Synchronous on the null stream: synchronize the streams of the
+ * checked calls first.  For callers that cannot trust their page tables (debugging). */
+int32_t mla_checked_bad_pages(void);
 
 /* Static description of a status code (never NULL). */
 const char* mla_status_str(mla_status_t status);

@@ -46,6 +46,19 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) <= exported
 
 
+def test_checked_library_exports_every_declared_symbol():
+    """libmla_checked.so is the same library with device-side page-table checks."""
+    assert os.path.exists(mla.CHECKED_LIB_PATH)
+    lib = mla.load(checked=True)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_unchecked_library_reports_no_checks():
+    # returns before any HIP call in libmla.so
+    assert mla.mla_checked_bad_pages(checked=False) == -1
+
+
 def test_shape_struct_layout():
     assert ctypes.sizeof(mla.MlaShape) == 15 * 4
 

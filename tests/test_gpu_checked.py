@@ -1,0 +1,119 @@
+"""libmla_checked.so on the GPU: page-table entries outside [0, num_pages) are never used as
+addresses, raise the bad-page flag (mla_checked_bad_pages), and leave every other
+sequence's results equal to the oracle's.  Only the checked library is ever given a
+corrupted page table."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import head_latent_attention_02_amd as mla
+from oracle import mla as ref
+from workloads import get_config, make_inputs
+from workloads.device import DeviceInputs
+from workloads.gen import bf16_round
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+CTX = ("list", [700, 300, 129])   # sequence 1 spans 5 pages
+BAD = 1                           # the sequence whose page entries are corrupted
+
+
+def rel_err(got, want):
+    got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isneginf(got), np.isneginf(want)), "-inf pattern differs"
+    assert np.all(np.isfinite(got[fin]))
+    return float(np.max(np.abs(got[fin] - want[fin])) / np.max(np.abs(want[fin])))
+
+
+def corrupt(d):
+    """Sequence BAD's first two page entries: one past the pool, one negative."""
+    d.page_table[BAD, 0] = d.shape.num_pages + 3
+    d.page_table[BAD, 1] = -5
+    torch.cuda.synchronize()
+
+
+def stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+@pytest.mark.parametrize("name", ["dsv2-b16-t4096", "gqla-b32-t8192", "tiny-f32"])
+def test_absorbed_decode_flags_out_of_range_pages(name):
+    """64-row and 32-row matrix-core kernels and the generic kernel."""
+    cfg = get_config(name, batch=3, ctx=CTX, n_splits=3)
+    inp = make_inputs(cfg, seed=31)
+    d = DeviceInputs(inp)
+    lib = mla.load(checked=True)
+    mla.mla_checked_bad_pages()                       # clear
+    mla.mla_absorb_q(d.shape, d.q, d.w_uk, d.q_abs)   # reads no page table
+    op = d.o_part_view(cfg.d_c)
+
+    def run():
+        st = lib.mla_decode_absorbed(ctypes.byref(d.shape), d.q_abs.data_ptr(),
+                                     d.pool.data_ptr(), d.page_table.data_ptr(),
+                                     d.ctx_lens.data_ptr(), op.data_ptr(),
+                                     d.lse_part.data_ptr(), stream())
+        assert st == mla.MLA_OK
+        torch.cuda.synchronize()
+        return op.cpu().numpy(), d.lse_part.cpu().numpy()
+
+    q_abs = ref.absorb_query(inp.q, inp.w_uk, cfg.d_nope)
+    o_p, l_p = ref.absorbed_split_partials(q_abs, inp.pool_view(), inp.page_table,
+                                           inp.ctx_lens, 3, cfg.scale, cfg.page_size, cfg.d_c,
+                                           d.shape.split_tokens)
+    got, got_l = run()
+    assert mla.mla_checked_bad_pages() == 0
+    assert rel_err(got, o_p) <= TOL[cfg.dtype] and rel_err(got_l, l_p) <= TOL[cfg.dtype]
+
+    corrupt(d)
+    got, got_l = run()
+    assert mla.mla_checked_bad_pages() == 1
+    assert mla.mla_checked_bad_pages() == 0           # the query clears the flag
+    keep = [b for b in range(cfg.batch) if b != BAD]
+    assert rel_err(got[keep], o_p[keep]) <= TOL[cfg.dtype]
+    assert rel_err(got_l[keep], l_p[keep]) <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("name", ["gqla-b32-t8192", "tiny-f32"])
+def test_gqa_decode_flags_out_of_range_pages(name):
+    """The GQA path: matrix-core kernel (bf16 GQLA shape) and generic kernel (fp32)."""
+    cfg = get_config(name, batch=3, ctx=CTX, n_splits=3)
+    inp = make_inputs(cfg, seed=32)
+    ek, ev, ekr = ref.expand_cache(inp.pool_f32(), inp.w_uk, inp.w_uv, cfg.d_c)
+    if cfg.dtype == "bf16":
+        k_np, v_np, kr_np = (bf16_round(x.astype(np.float32)) for x in (ek, ev, ekr))
+        tdt = torch.bfloat16
+    else:
+        k_np, v_np, kr_np = (x.astype(np.float32) for x in (ek, ev, ekr))
+        tdt = torch.float32
+    d = DeviceInputs(inp)
+    k, v, kr = (torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda().to(tdt)
+                for x in (k_np, v_np, kr_np))
+    lib = mla.load(checked=True)
+    mla.mla_checked_bad_pages()
+    op = d.o_part_view(cfg.d_v)
+
+    def run():
+        st = lib.gqla_decode_gqa(ctypes.byref(d.shape), d.q.data_ptr(), k.data_ptr(),
+                                 v.data_ptr(), kr.data_ptr(), d.page_table.data_ptr(),
+                                 d.ctx_lens.data_ptr(), op.data_ptr(), d.lse_part.data_ptr(),
+                                 stream())
+        assert st == mla.MLA_OK
+        torch.cuda.synchronize()
+        return op.cpu().numpy(), d.lse_part.cpu().numpy()
+
+    o_p, l_p = ref.gqa_split_partials(inp.q, k_np, v_np, kr_np, inp.page_table, inp.ctx_lens,
+                                      3, cfg.scale, cfg.page_size)
+    got, got_l = run()
+    assert mla.mla_checked_bad_pages() == 0
+    assert rel_err(got, o_p) <= TOL[cfg.dtype] and rel_err(got_l, l_p) <= TOL[cfg.dtype]
+
+    corrupt(d)
+    got, got_l = run()
+    assert mla.mla_checked_bad_pages() == 1
+    keep = [b for b in range(cfg.batch) if b != BAD]
+    assert rel_err(got[keep], o_p[keep]) <= TOL[cfg.dtype]
+    assert rel_err(got_l[keep], l_p[keep]) <= TOL[cfg.dtype]
