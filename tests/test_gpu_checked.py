@@ -117,3 +117,26 @@ def test_gqa_decode_flags_out_of_range_pages(name):
     keep = [b for b in range(cfg.batch) if b != BAD]
     assert rel_err(got[keep], o_p[keep]) <= TOL[cfg.dtype]
     assert rel_err(got_l[keep], l_p[keep]) <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("name", ["long-b4-t131072", "gqla-b32-t8192"])
+def test_checked_library_matches_unchecked_on_valid_tables(name):
+    """With every page entry valid, the checked build computes exactly what libmla.so does
+    (the checks only select addresses), through the whole step."""
+    kw = dict(batch=2, ctx=("list", [9000, 1500])) if name.startswith("long") else dict(batch=3)
+    cfg = get_config(name, **kw)
+    d = DeviceInputs(make_inputs(cfg, seed=33))
+    outs = []
+    for checked in (False, True):
+        lib = mla.load(checked=checked)
+        d.out.fill_(7.0)
+        st = lib.mla_decode_step(ctypes.byref(d.shape), d.q.data_ptr(), d.w_uk.data_ptr(),
+                                 d.w_uv.data_ptr(), d.pool.data_ptr(), d.page_table.data_ptr(),
+                                 d.ctx_lens.data_ptr(), d.q_abs.data_ptr(), d.o_part.data_ptr(),
+                                 d.lse_part.data_ptr(), d.o_lat.data_ptr(), d.out.data_ptr(),
+                                 d.lse.data_ptr(), stream())
+        assert st == mla.MLA_OK
+        torch.cuda.synchronize()
+        outs.append((d.out.clone(), d.lse.clone()))
+    assert mla.mla_checked_bad_pages() == 0
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
