@@ -31,6 +31,20 @@ __device__ __forceinline__ int checked_page(int page, int num_pages, unsigned in
   return page;
 }
 
+// Checked builds also bound each device-resident context length T_b to [0, max_tokens]
+// (max_tokens = max_pages * page_size, the tokens one page-table row can map) before it
+// becomes a page-table index, and raise the same flag when they have to clamp it, so a
+// length past the table row never reads beyond that row.  Unchecked builds use T_b as is.
+__device__ __forceinline__ int checked_len(int T, int max_tokens, unsigned int* bad) {
+  if constexpr (kChecked) {
+    if (T < 0 || T > max_tokens) {
+      if (bad) *bad = 1u;
+      return T < 0 ? 0 : max_tokens;
+    }
+  }
+  return T;
+}
+
 __device__ __forceinline__ float ldf(const float* p) { return *p; }
 __device__ __forceinline__ float ldf(const bf16_t* p) {
   return __uint_as_float(static_cast<uint32_t>(*p) << 16);

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void decode_absorbed_generic_kernel(
   const int row = blockIdx.y * 4 + (threadIdx.x >> 6);  // row = s * H + h
   if (row >= s_q * H) return;                            // no barrier in this kernel
   const int s = row / H, h = row - s * H;
-  const int n_ctx = lens[b];
+  const int n_ctx = checked_len(lens[b], max_pages * P, bad);
   int lo, hi;
   split_range(n_ctx, u, S, P, split_tokens, lo, hi);
   const int top = min(hi, n_ctx - s_q + s + 1);
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void gqa_decode_generic_kernel(
   if (row >= s_q * H) return;
   const int s = row / H, h = row - s * H;
   const int j = h / (H / G);
-  const int n_ctx = lens[b];
+  const int n_ctx = checked_len(lens[b], max_pages * P, bad);
   int lo, hi;
   split_range(n_ctx, u, S, P, split_tokens, lo, hi);
   const int top = min(hi, n_ctx - s_q + s + 1);

@@ -697,7 +697,7 @@ __device__ __forceinline__ void value_wave128(Smem& sm, const Work& w, int lane)
     if (unit >= n_units) return;                                                   \
     const int b = unit / S;                                                        \
     w.u = unit - b * S;                                                            \
-    w.T = lens[b];                                                                 \
+    w.T = checked_len(lens[b], max_pages * kPage, bad);                            \
     split_range(w.T, w.u, S, kPage, split_tokens, w.lo, w.hi);                     \
     w.n_tiles = (w.hi > w.lo) ? (w.hi - w.lo + kTT - 1) / kTT : 0;                 \
     w.q_abs = q_abs;                                                               \

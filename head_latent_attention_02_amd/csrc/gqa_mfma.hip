@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_mfma_kernel(
   const int unit = (rest / G) * 8 + (wg & 7);
   if (unit >= n_units) return;   // uniform for the workgroup, before any barrier
   const int b = unit / S, u = unit - b * S;
-  const int T = lens[b];
+  const int T = checked_len(lens[b], max_pages * kPage, bad);
   Args a;
   a.k = kpool;
   a.v = vpool;

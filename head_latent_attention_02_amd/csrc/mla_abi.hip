@@ -12,6 +12,14 @@ namespace {
 // The bad-page flag of checked builds (see checked_page): one word per device, set by the
 // decode kernels, read and cleared by mla_checked_bad_pages.
 __device__ unsigned int g_bad_pages;
+// Where mla_checked_bad_pages's kernel leaves the value it swapped out of g_bad_pages.
+__device__ unsigned int g_bad_pages_taken;
+
+// Reads and clears the flag in one atomic exchange, so a flag that a checked kernel still
+// running on another stream raises is either returned now or kept for the next query.
+__global__ void take_bad_pages_kernel(unsigned int* flag, unsigned int* taken) {
+  *taken = atomicExch(flag, 0u);
+}
 
 // This device's flag for the kernels (checked builds), nullptr if it cannot be found.
 unsigned int* bad_page_flag() {
@@ -46,10 +54,17 @@ mla_status_t validate(const mla_shape_t* s) {
         static_cast<int64_t>(s->max_pages) * s->page_size)
       return MLA_ERR_SHAPE;
   }
-  // grid dimensions used by the launchers
-  if (s->batch > 65535 || (s->s_q * static_cast<int64_t>(s->n_heads) + 3) / 4 > 65535 ||
-      s->n_splits > 65535)
+  // grid dimensions used by the launchers: y and z extents stay within 65535, and every
+  // one-dimensional grid (workgroups x threads) within 2^31 threads
+  const int64_t rows = static_cast<int64_t>(s->s_q) * s->n_heads;   // query rows per sequence
+  const int64_t units = static_cast<int64_t>(s->batch) * s->n_splits;
+  const int64_t row_blocks = (rows + 31) / 32;
+  if (s->batch > 65535 || (rows + 3) / 4 > 65535 || s->n_splits > 65535)
     return MLA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(s->batch) * s->s_q > 262140) return MLA_ERR_UNSUPPORTED;
+  if (rows * s->batch > (int64_t{1} << 24)) return MLA_ERR_UNSUPPORTED;   // merge: 128 threads/row
+  const int64_t per_unit = row_blocks > s->n_wheads ? row_blocks : s->n_wheads;
+  if (((units + 7) / 8) * 8 * per_unit > (int64_t{1} << 22)) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 
@@ -218,13 +233,16 @@ mla_status_t gqla_decode_step(const mla_shape_t* s, const void* q, const void* k
 
 int32_t mla_checked_bad_pages(void) {
   if (!mla::kChecked) return -1;
+  void* flag = nullptr;
+  void* taken = nullptr;
+  if (hipGetSymbolAddress(&flag, HIP_SYMBOL(g_bad_pages)) != hipSuccess ||
+      hipGetSymbolAddress(&taken, HIP_SYMBOL(g_bad_pages_taken)) != hipSuccess)
+    return -2;
+  hipLaunchKernelGGL(take_bad_pages_kernel, dim3(1), dim3(1), 0, 0,
+                     static_cast<unsigned int*>(flag), static_cast<unsigned int*>(taken));
+  if (hipGetLastError() != hipSuccess) return -2;
   unsigned int v = 0;
-  const unsigned int zero = 0;
-  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_bad_pages), sizeof(v), 0, hipMemcpyDeviceToHost) !=
-      hipSuccess)
-    return -2;
-  if (hipMemcpyToSymbol(HIP_SYMBOL(g_bad_pages), &zero, sizeof(zero), 0,
-                        hipMemcpyHostToDevice) != hipSuccess)
-    return -2;
+  // synchronous on the null stream: waits for the exchange kernel
+  if (hipMemcpy(&v, taken, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return -2;
   return v ? 1 : 0;
 }

@@ -16,7 +16,8 @@
  *
  * Conventions shared by every entry point
  *  - All tensor arguments are DEVICE pointers owned by the caller; the library allocates
- *    nothing, keeps no global state and never synchronises.  Every call is asynchronous
+ *    nothing and never synchronises (the checked build's bad-page flag, below, is its only
+ *    global state, and mla_checked_bad_pages its only synchronous call).  Every call is asynchronous
  *    on `stream` (0 = the null stream).  Tensors are dense, row-major, in the layouts
  *    given below; `dtype` (MLA_F32 or MLA_BF16) is the element type of q, q_abs, the
  *    caches and the weights.  Split partials, latent outputs and final outputs are fp32.
@@ -28,8 +29,9 @@
  *    0 <= T_b <= max_pages * page_size and 0 <= page_table[b][i] < num_pages for
  *    i < ceil(T_b / page_size); entries past that are never read (use -1).  libmla.so
  *    does not validate these device values: breaking them is undefined behaviour.  The
- *    checked build libmla_checked.so bounds-checks page-table entries (see
- *    mla_checked_bad_pages).
+ *    checked build libmla_checked.so bounds-checks both on the device: a length outside
+ *    [0, max_pages * page_size] is clamped into it and a page entry outside [0, num_pages)
+ *    is replaced by page 0, and either raises the flag that mla_checked_bad_pages reports.
  *  - Split-KV: sequence b is cut into n_splits chunks.  split_tokens == 0: chunk length
  *    L_b = ceil(ceil(T_b / n_splits) / page_size) * page_size; split_tokens > 0: fixed
  *    L = split_tokens (a multiple of page_size, and n_splits * L must cover
@@ -196,13 +198,16 @@ int32_t mla_decode_kernel_kind(const mla_shape_t* shape);
 int32_t gqla_decode_kernel_kind(const mla_shape_t* shape);
 
 /* Checked builds only.  libmla_checked.so (the same sources compiled with MLA_CHECKED)
- * bounds-checks every page-table entry that the decode entry points (a2, a5 and the two step
- * helpers) read on the device: an entry outside [0, num_pages) is replaced by page 0, so
- * nothing outside the pool is read, and sets a per-device flag; the outputs of such a call
- * are meaningless.  Returns 1 if the current device's flag was set since the last call, else
- * 0, and clears it; -1 in libmla.so (no checks; out-of-range entries are undefined behaviour
- * there); -2 on a HIP error.  Synchronous on the null stream: synchronize the streams of the
- * checked calls first.  For callers that cannot trust their page tables (debugging). */
+ * bounds-checks the device data that the decode entry points (a2, a5 and the two step
+ * helpers) read: a context length outside [0, max_pages * page_size] is clamped into that
+ * range before it indexes the page table, and a page-table entry outside [0, num_pages) is
+ * replaced by page 0, so nothing outside the table row or the pool is read.  Either sets a
+ * per-device flag; the outputs of such a call are meaningless.  Returns 1 if the current
+ * device's flag was set since the last call, else 0, and clears it (read and clear are one
+ * atomic exchange on the device); -1 in libmla.so (no checks; such values are undefined
+ * behaviour there); -2 on a HIP error.  Synchronous on the null stream: synchronize the
+ * streams of the checked calls first, or a flag they raise later is reported by the next
+ * query.  For callers that cannot trust their page tables or lengths (debugging). */
 int32_t mla_checked_bad_pages(void);
 
 /* Static description of a status code (never NULL). */

@@ -93,6 +93,12 @@ def test_cache_sizes_match_oracle_and_pages():
     (dict(split_tokens=100), mla.MLA_ERR_SHAPE),
     (dict(split_tokens=64, n_splits=3), mla.MLA_ERR_SHAPE),
     (dict(max_pages=0), mla.MLA_ERR_SHAPE),
+    # products of individually valid sizes that would overflow a launch grid
+    (dict(batch=65535, n_splits=65535), mla.MLA_ERR_UNSUPPORTED),
+    (dict(batch=40000, s_q=8, n_heads=128, n_wheads=128), mla.MLA_ERR_UNSUPPORTED),
+    (dict(batch=4096, s_q=1, n_heads=8192, n_wheads=8192, n_splits=1),
+     mla.MLA_ERR_UNSUPPORTED),
+    (dict(batch=65535, s_q=5), mla.MLA_ERR_UNSUPPORTED),
 ])
 def test_invalid_shapes_rejected_before_any_hip_call(bad, status):
     s = good_shape(**bad)

@@ -1,7 +1,8 @@
 """libmla_checked.so on the GPU: page-table entries outside [0, num_pages) are never used as
-addresses, raise the bad-page flag (mla_checked_bad_pages), and leave every other
-sequence's results equal to the oracle's.  Only the checked library is ever given a
-corrupted page table."""
+addresses and context lengths outside [0, max_pages * page_size] are clamped before they
+index the page table; either raises the bad-page flag (mla_checked_bad_pages) and leaves
+every other sequence's results equal to the oracle's.  Only the checked library is ever
+given a corrupted page table or length."""
 import ctypes
 
 import numpy as np
@@ -140,3 +141,72 @@ def test_checked_library_matches_unchecked_on_valid_tables(name):
         outs.append((d.out.clone(), d.lse.clone()))
     assert mla.mla_checked_bad_pages() == 0
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def _bad_len(d, kind):
+    """A context length the page table cannot map: past max_pages * page_size, or negative."""
+    return d.shape.max_pages * d.shape.page_size + 777 if kind == "long" else -5
+
+
+@pytest.mark.parametrize("kind", ["long", "negative"])
+@pytest.mark.parametrize("name", ["dsv2-b16-t4096", "gqla-b32-t8192", "tiny-f32"])
+def test_absorbed_decode_clamps_out_of_range_lengths(name, kind):
+    """A length outside [0, max_pages * page_size] is clamped on the device before it
+    indexes the page table (only libmla_checked.so is given one): the flag is raised and
+    every other sequence still matches the oracle."""
+    cfg = get_config(name, batch=3, ctx=CTX, n_splits=3)
+    inp = make_inputs(cfg, seed=34)
+    d = DeviceInputs(inp)
+    lib = mla.load(checked=True)
+    mla.mla_checked_bad_pages()
+    mla.mla_absorb_q(d.shape, d.q, d.w_uk, d.q_abs)
+    op = d.o_part_view(cfg.d_c)
+    q_abs = ref.absorb_query(inp.q, inp.w_uk, cfg.d_nope)
+    o_p, l_p = ref.absorbed_split_partials(q_abs, inp.pool_view(), inp.page_table,
+                                           inp.ctx_lens, 3, cfg.scale, cfg.page_size, cfg.d_c,
+                                           d.shape.split_tokens)
+    d.ctx_lens[BAD] = _bad_len(d, kind)
+    torch.cuda.synchronize()
+    print(f"checked absorbed decode {name}: ctx_lens[{BAD}] = {_bad_len(d, kind)}", flush=True)
+    st = lib.mla_decode_absorbed(ctypes.byref(d.shape), d.q_abs.data_ptr(), d.pool.data_ptr(),
+                                 d.page_table.data_ptr(), d.ctx_lens.data_ptr(), op.data_ptr(),
+                                 d.lse_part.data_ptr(), stream())
+    assert st == mla.MLA_OK
+    torch.cuda.synchronize()
+    assert mla.mla_checked_bad_pages() == 1
+    got, got_l = op.cpu().numpy(), d.lse_part.cpu().numpy()
+    keep = [b for b in range(cfg.batch) if b != BAD]
+    assert rel_err(got[keep], o_p[keep]) <= TOL[cfg.dtype]
+    assert rel_err(got_l[keep], l_p[keep]) <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("kind", ["long", "negative"])
+@pytest.mark.parametrize("name", ["gqla-b32-t8192", "tiny-f32"])
+def test_gqa_decode_clamps_out_of_range_lengths(name, kind):
+    cfg = get_config(name, batch=3, ctx=CTX, n_splits=3)
+    inp = make_inputs(cfg, seed=35)
+    ek, ev, ekr = ref.expand_cache(inp.pool_f32(), inp.w_uk, inp.w_uv, cfg.d_c)
+    conv = bf16_round if cfg.dtype == "bf16" else (lambda x: x)
+    k_np, v_np, kr_np = (conv(x.astype(np.float32)) for x in (ek, ev, ekr))
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    d = DeviceInputs(inp)
+    k, v, kr = (torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda().to(tdt)
+                for x in (k_np, v_np, kr_np))
+    lib = mla.load(checked=True)
+    mla.mla_checked_bad_pages()
+    op = d.o_part_view(cfg.d_v)
+    o_p, l_p = ref.gqa_split_partials(inp.q, k_np, v_np, kr_np, inp.page_table, inp.ctx_lens,
+                                      3, cfg.scale, cfg.page_size)
+    d.ctx_lens[BAD] = _bad_len(d, kind)
+    torch.cuda.synchronize()
+    print(f"checked GQA decode {name}: ctx_lens[{BAD}] = {_bad_len(d, kind)}", flush=True)
+    st = lib.gqla_decode_gqa(ctypes.byref(d.shape), d.q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             kr.data_ptr(), d.page_table.data_ptr(), d.ctx_lens.data_ptr(),
+                             op.data_ptr(), d.lse_part.data_ptr(), stream())
+    assert st == mla.MLA_OK
+    torch.cuda.synchronize()
+    assert mla.mla_checked_bad_pages() == 1
+    got, got_l = op.cpu().numpy(), d.lse_part.cpu().numpy()
+    keep = [b for b in range(cfg.batch) if b != BAD]
+    assert rel_err(got[keep], o_p[keep]) <= TOL[cfg.dtype]
+    assert rel_err(got_l[keep], l_p[keep]) <= TOL[cfg.dtype]
