@@ -73,6 +73,8 @@ def parse():
     ap.add_argument("--flush", choices=("read", "write"), default="read",
                     help="how the last-level cache is flushed between steps (read: sum a "
                          "1 GiB buffer; write: fill it)")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the measured HBM-read and MFMA peaks (libmla_calib.so)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -87,6 +89,80 @@ def copy_calibration():
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n}))
+
+
+def measured_peaks():
+    """The machine's own roofline denominators from libmla_calib.so: a pure HBM read stream
+    (every workgroup its own contiguous span, 1 KB per load instruction, non-temporal; the
+    best of 5 launches over a 604 MB buffer) and a dense bf16 v_mfma_f32_32x32x16 loop (the
+    best of 5), both timed with HIP events on the launch stream."""
+    import ctypes
+    import torch
+    from head_latent_attention_02_amd.build import CALIB_LIB_PATH
+    if not os.path.exists(CALIB_LIB_PATH):
+        return None
+    lib = ctypes.CDLL(CALIB_LIB_PATH)
+    lib.calib_hbm_read_bytes.restype = ctypes.c_int64
+    lib.calib_hbm_read_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.calib_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    lib.calib_mfma_bf16_flops.restype = ctypes.c_int64
+    lib.calib_mfma_bf16_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.calib_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    st = torch.cuda.current_stream()
+    n_wg, tiles = 256, 64
+    nbytes = lib.calib_hbm_read_bytes(n_wg, tiles)
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty(n_wg * 256, dtype=torch.int32, device="cuda")
+    flush = _flusher()
+
+    def best_ms(launch, reps=5):
+        out = []
+        for _ in range(reps + 1):
+            flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            if launch() != 0:
+                raise RuntimeError("calibration launch failed")
+            b.record(st)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b))
+        return min(out[1:])
+
+    hbm_ms = best_ms(lambda: lib.calib_hbm_read(buf.data_ptr(), n_wg, tiles, sink.data_ptr(),
+                                                st.cuda_stream))
+    del buf
+    m_wg, iters = 512, 20000
+    fsink = torch.empty(m_wg * 256, dtype=torch.float32, device="cuda")
+    mfma_ms = best_ms(lambda: lib.calib_mfma_bf16(m_wg, iters, fsink.data_ptr(),
+                                                  st.cuda_stream))
+    return {"hbm_read_GBs": nbytes / (hbm_ms * 1e-3) / 1e9,
+            "mfma_bf16_TFLOPs": lib.calib_mfma_bf16_flops(m_wg, iters) / (mfma_ms * 1e-3) / 1e12,
+            "source": "libmla_calib.so (calib/calib.hip): 604 MB non-temporal read stream, "
+                      "dense 32x32x16 bf16 MFMA loop; best of 5 launches each"}
+
+
+def host_info():
+    """CPU model and the BLAS library numpy uses, for the CPU baseline's record."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:
+        pass
+    return model, blas
 
 
 def cpu_baseline(inp, seconds):
@@ -112,8 +188,9 @@ def cpu_baseline(inp, seconds):
     el = time.perf_counter() - t0
     per_row = el / done                     # one (sequence, head) row over T_0 tokens
     step_s = per_row * c.batch * c.n_heads * float(np.mean(inp.ctx_lens)) / float(inp.ctx_lens[0])
+    model, blas = host_info()
     return {"value": inp.total_tokens / step_s, "unit": "cached-latent-tokens/s",
-            "cores": int(cores), "kind": "oracle",
+            "cores": int(cores), "kind": "oracle", "cpu_model": model, "blas": blas,
             "sample": f"{done} (sequence 0, head) rows of {int(inp.ctx_lens[0])} tokens in "
                       f"{el:.1f} s, scaled to all {c.batch}x{c.n_heads} rows"}
 
@@ -345,12 +422,17 @@ def main():
     dec_bytes = tokens * c.D * 2                                  # algorithmic cache bytes
     dec_flops = tokens * c.s_q * c.n_heads * (2 * c.D + 2 * c.d_c)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
-    traffic = None
+    traffic, traffic_source = None, None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_sha") == kernel_hash() and tr.get("workload") == args.workload:
             traffic = tr.get("hbm_bytes_per_launch")
+            # not measured in this run: read from the committed counter record, which holds
+            # rocprofv3 FETCH_SIZE / WRITE_SIZE of the same kernel source on this workload
+            traffic_source = (os.path.relpath(TRAFFIC_FILE, ROOT) + " (rocprofv3 FETCH_SIZE "
+                              "and WRITE_SIZE taken on kernel source " + tr["kernel_sha"] + ")")
+    peaks = None if args.no_calibration else measured_peaks()
     line = {
         "metric": "MLA decode cached-latent-tokens/s; % HBM-BW and % bf16 MFMA peak, 1 GPU",
         "value": tokens / (ms_step * 1e-3),
@@ -372,10 +454,16 @@ def main():
         "wall_ms_per_step_incl_flushes_and_kernel_pass": wall_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_source": traffic_source,
                      "kernel": "mla_decode_absorbed", "kernel_ms": dec_ms,
                      "mfma_tflops": dec_flops / (dec_ms * 1e-3) / 1e12,
                      "mfma_frac": dec_flops / (dec_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
     }
+    if peaks:
+        line["roofline"]["measured_peak"] = peaks
+        line["roofline"]["frac_of_measured_hbm"] = achieved / peaks["hbm_read_GBs"]
+        line["roofline"]["mfma_frac_of_measured"] = (
+            dec_flops / (dec_ms * 1e-3) / 1e12 / peaks["mfma_bf16_TFLOPs"])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -154,6 +154,19 @@ def test_softmax_rows_are_distributions():
         assert len(p) == int(inp.ctx_lens[b]) - cfg.s_q + s + 1
 
 
+def test_softmax_stats_match_scipy():
+    """The oracle's softmax and log-sum-exp equal scipy's independent routines, including
+    logits far outside exp's range (the max-shift must be right)."""
+    from scipy.special import logsumexp, softmax
+    rng = np.random.default_rng(5)
+    for n, spread, shift in [(1, 1.0, 0.0), (7, 3.0, 0.0), (300, 20.0, 900.0),
+                             (64, 50.0, -800.0), (1000, 0.6, 0.0)]:
+        z = rng.normal(shift, spread, size=n)
+        p, lse = mla._softmax_stats(z)
+        assert abs(lse - logsumexp(z)) <= 1e-12 * max(1.0, abs(lse))
+        np.testing.assert_allclose(p, softmax(z), rtol=1e-12, atol=1e-300)
+
+
 # ------------------------------------------------------------- the two equivalences
 
 @pytest.mark.parametrize("s_q,Hw,S,split_tokens", [
