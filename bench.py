@@ -66,8 +66,9 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--extra", action="store_true",
                     help="also time the other workloads (stderr lines)")
-    ap.add_argument("--path", choices=("absorbed", "gqa"), default="absorbed",
-                    help="absorbed MLA step (default) or the GQLA per-group GQA path")
+    ap.add_argument("--path", choices=("absorbed", "gqa", "expand"), default="absorbed",
+                    help="absorbed MLA step (default), the GQLA per-group GQA path, or the "
+                         "GQA path's cache expansion alone (a stderr-style JSON line)")
     ap.add_argument("--no-flush", action="store_true",
                     help="do not flush the last-level cache between steps")
     ap.add_argument("--flush", choices=("read", "write"), default="read",
@@ -344,6 +345,53 @@ def time_gqa_path(name, steps, warmup, flush=True):
             "kernel": "mfma" if mla.gqla_decode_kernel_kind(sh) == 1 else "generic"}
 
 
+def time_expand(name, steps, warmup, flush=True):
+    """a6, the GQA path's set-up: the per-group K, V and shared RoPE-key cache built from the
+    latent cache (every pool row, padding included), timed alone with events around it."""
+    import torch
+    import head_latent_attention_02_amd as mla
+    from workloads import get_config, make_inputs
+    from workloads.device import DeviceInputs
+
+    cfg = get_config(name)
+    inp = make_inputs(cfg)
+    d = DeviceInputs(inp)
+    n = inp.num_pages
+    k = torch.empty(n, cfg.page_size, cfg.n_wheads, cfg.d_nope, dtype=torch.bfloat16,
+                    device="cuda")
+    v = torch.empty(n, cfg.page_size, cfg.n_wheads, cfg.d_v, dtype=torch.bfloat16,
+                    device="cuda")
+    kr = torch.empty(n, cfg.page_size, cfg.d_rope, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    fl = _flusher() if flush else (lambda: None)
+
+    def step():
+        mla.gqla_expand_cache(d.shape, d.pool, d.w_uk, d.w_uv, k, v, kr,
+                              stream=stream.cuda_stream)
+
+    for _ in range(warmup):
+        fl()
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        fl()
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms, p10, p90 = _stats([e[0].elapsed_time(e[1]) for e in evs])
+    rows = n * cfg.page_size
+    wbytes = rows * (cfg.n_wheads * (cfg.d_nope + cfg.d_v) + cfg.d_rope) * 2
+    rbytes = rows * cfg.D * 2
+    flops = 2.0 * rows * cfg.n_wheads * (cfg.d_nope + cfg.d_v) * cfg.d_c
+    return {"workload": name, "path": "expand", "ms": ms, "ms_p10_p90": [p10, p90],
+            "rows": rows, "bytes_written": wbytes, "bytes_read": rbytes,
+            "write_GBs": wbytes / (ms * 1e-3) / 1e9,
+            "hbm_GBs": (wbytes + rbytes) / (ms * 1e-3) / 1e9,
+            "mfma_TFLOPs": flops / (ms * 1e-3) / 1e12}
+
+
 def time_append(name, steps, warmup, d_model=5120, flush=True):
     """Cache-append step (write side): the step's new tokens projected, rotated and
     written into the paged cache."""
@@ -395,6 +443,11 @@ def main():
         return
     import head_latent_attention_02_amd as mla
 
+    if args.path == "expand":
+        name = args.workload if args.workload.startswith("gqla") else "gqla-b32-t65536"
+        print(json.dumps(time_expand(name, args.steps, min(args.warmup, 20),
+                                     flush=not args.no_flush)), flush=True)
+        return
     if args.path == "gqa":
         g = time_gqa_path(args.workload, args.steps, args.warmup, flush=not args.no_flush)
         ach = g["decode_GBs"]
@@ -487,6 +540,8 @@ def main():
             print(json.dumps(time_gqa_path(name, args.steps, args.warmup,
                                            flush=not args.no_flush)),
                   file=sys.stderr, flush=True)
+        print(json.dumps(time_expand("gqla-b32-t65536", args.steps, min(args.warmup, 20),
+                                     flush=not args.no_flush)), file=sys.stderr, flush=True)
         for name in ("long-b4-t131072", "mtp-b64-ragged"):
             print(json.dumps(time_append(name, args.steps, args.warmup,
                                          flush=not args.no_flush)),

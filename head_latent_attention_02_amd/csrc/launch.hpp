@@ -45,5 +45,10 @@ hipError_t launch_cache_append(const mla_shape_t& s, int d_model, float rope_bas
 hipError_t launch_expand_cache(const mla_shape_t& s, const void* pool, const void* w_uk,
                                const void* w_uv, void* k, void* v, void* kr,
                                hipStream_t st);
+// a6 on the matrix cores (bf16, d_c 512, d_nope = d_v = 128)
+bool expand_cache_mfma_supported(const mla_shape_t& s);
+hipError_t launch_expand_cache_mfma(const mla_shape_t& s, const void* pool, const void* w_uk,
+                                    const void* w_uv, void* k, void* v, void* kr,
+                                    hipStream_t st);
 
 }  // namespace mla

@@ -808,6 +808,8 @@ hipError_t launch_combine_out_uv(const mla_shape_t& s, const float* o_part,
 hipError_t launch_expand_cache(const mla_shape_t& s, const void* pool, const void* w_uk,
                                const void* w_uv, void* k, void* v, void* kr,
                                hipStream_t st) {
+  if (expand_cache_mfma_supported(s))
+    return launch_expand_cache_mfma(s, pool, w_uk, w_uv, k, v, kr, st);
   dim3 grid(s.num_pages, s.n_wheads, (s.d_nope + s.d_v + kEO - 1) / kEO);
   if (s.dtype == MLA_F32)
     hipLaunchKernelGGL(expand_kernel<float>, grid, dim3(256), 0, st,
