@@ -16,6 +16,8 @@ Everything here is plain numpy in float64, written from the pages' definitions:
               used to pin ``mla`` against an independent implementation.
 * ``append`` - the cache-append step on the write side: latent down-projection, RoPE
               key projection and rotation, paged write of the new tokens' rows.
+* ``projections`` - the query projection from the hidden state and the output projection
+              back to it, unfolded and with W_UK / W_UV folded into them offline.
 
 Parity status: every function in ``mla`` is pinned by tests/test_oracle.py against
 something other than itself (pure-Python brute force, torch's scaled-dot-product
@@ -23,7 +25,9 @@ attention as a library routine, closed forms for special cases, the absorbed/exp
 and MQA-absorb/GQA-path equivalences the pages state, and the cache sizes the pages
 print); every function in ``append`` by tests/test_oracle_append.py (the rotation's
 group properties, a complex-number formulation, pure-Python loops, closed forms and the
-positions the decode path's visibility rule fixes).  No function here is "parity
+positions the decode path's visibility rule fixes); every function in ``projections`` by
+tests/test_oracle_projections.py (associativity of the fold, pure-Python loops, identity
+weights, and the whole step through the naive decode).  No function here is "parity
 unpinned".
 """
-from . import mla, brute, append  # noqa: F401
+from . import mla, brute, append, projections  # noqa: F401

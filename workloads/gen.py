@@ -187,3 +187,31 @@ def make_append_inputs(cfg: Config, d_model=5120, seed=None):
     if bf16:
         w_dkv, w_kr = bf16_round(w_dkv), bf16_round(w_kr)
     return AppendInputs(h, w_dkv, w_kr)
+
+
+class ProjectionInputs:
+    """Inputs of the projections around the decode path: the new tokens' hidden states, the
+    query weights and the output projection (float32; bf16-exact for bf16 workloads)."""
+
+    def __init__(self, x, w_q, w_o):
+        self.x, self.w_q, self.w_o = x, w_q, w_o
+        self.d_model = x.shape[-1]
+
+
+def make_projection_inputs(cfg: Config, d_model=5120, seed=None):
+    """Seeded inputs of the query and output projections, from streams of their own
+    (``SeedSequence([seed, 2]).spawn(3)``) so the decode inputs of the same seed are
+    unchanged:  0 x ~ N(0, 1) [B, s_q, d_model];  1 W^Q ~ N(0, 1) / sqrt(d_model)
+    [H, d_nope + d_rope, d_model], so the query has unit variance like the drawn q;
+    2 W^O ~ N(0, 1) / sqrt(H d_v) [d_model, H d_v]."""
+    seed = cfg.seed if seed is None else seed
+    streams = [np.random.default_rng(x) for x in np.random.SeedSequence([seed, 2]).spawn(3)]
+    bf16 = cfg.dtype == "bf16"
+    x = _normal(streams[0], (cfg.batch, cfg.s_q, d_model), bf16)
+    w_q = _normal(streams[1], (cfg.n_heads, cfg.d_nope + cfg.d_rope, d_model), False)
+    w_q *= np.float32(1.0 / np.sqrt(d_model))
+    w_o = _normal(streams[2], (d_model, cfg.n_heads * cfg.d_v), False)
+    w_o *= np.float32(1.0 / np.sqrt(cfg.n_heads * cfg.d_v))
+    if bf16:
+        w_q, w_o = bf16_round(w_q), bf16_round(w_o)
+    return ProjectionInputs(x, w_q, w_o)
