@@ -66,7 +66,8 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--extra", action="store_true",
                     help="also time the other workloads (stderr lines)")
-    ap.add_argument("--path", choices=("absorbed", "gqa", "expand"), default="absorbed",
+    ap.add_argument("--path", choices=("absorbed", "gqa", "expand", "projections"),
+                    default="absorbed",
                     help="absorbed MLA step (default), the GQLA per-group GQA path, or the "
                          "GQA path's cache expansion alone (a stderr-style JSON line)")
     ap.add_argument("--no-flush", action="store_true",
@@ -392,6 +393,66 @@ def time_expand(name, steps, warmup, flush=True):
             "mfma_TFLOPs": flops / (ms * 1e-3) / 1e12}
 
 
+def time_projections(name, steps, warmup, d_model=5120, flush=True):
+    """Offline absorption measured against the runtime steps it replaces, on the workload's
+    batch: the query side as projection + a1 (W^Q then W_UK) versus the folded projection
+    (W~^Q, no a1), and the output side as a4 + projection (W_UV then W^O) versus the folded
+    projection (W~^O, no a4).  Each leg alone, events around it, cache flushed before it."""
+    import torch
+    import head_latent_attention_02_amd as mla
+    from workloads import get_config, make_inputs, make_projection_inputs
+    from workloads.device import DeviceInputs, to_dev
+
+    cfg = get_config(name, ctx=("list", [64] * get_config(name).batch))
+    inp = make_inputs(cfg)
+    pr = make_projection_inputs(cfg, d_model)
+    d = DeviceInputs(inp)
+    sh = d.shape
+    B, s_q, H = cfg.batch, cfg.s_q, cfg.n_heads
+    x, w_q, w_o = (to_dev(a, "bf16") for a in (pr.x, pr.w_q, pr.w_o))
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    q = torch.empty(B, s_q, H, cfg.d_nope + cfg.d_rope, **bf)
+    wqf = torch.empty(H, cfg.D, d_model, **bf)
+    wof = torch.empty(d_model, H * cfg.d_c, **bf)
+    y = torch.empty(B, s_q, d_model, dtype=torch.float32, device="cuda")
+    d.o_lat.normal_()
+    mla.mla_fold_q_weights(sh, d_model, w_q, d.w_uk, wqf)
+    mla.mla_fold_o_weights(sh, d_model, w_o, d.w_uv, wof)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    fl = _flusher() if flush else (lambda: None)
+    legs = {
+        "q_unfolded": lambda: (mla.mla_project_q(sh, d_model, 1e4, x, w_q, d.ctx_lens, q,
+                                                 stream=sp),
+                               mla.mla_absorb_q(sh, q, d.w_uk, d.q_abs, stream=sp)),
+        "q_folded": lambda: mla.mla_project_q_folded(sh, d_model, 1e4, x, wqf, d.ctx_lens,
+                                                     d.q_abs, stream=sp),
+        "o_unfolded": lambda: (mla.mla_out_uv(sh, d.o_lat, d.w_uv, d.out, stream=sp),
+                               mla.mla_out_project(sh, d_model, d.out, w_o, y, stream=sp)),
+        "o_folded": lambda: mla.mla_out_project_folded(sh, d_model, d.o_lat, wof, y,
+                                                       stream=sp),
+    }
+    wbytes = {"q_unfolded": (w_q.numel() + d.w_uk.numel()) * 2, "q_folded": wqf.numel() * 2,
+              "o_unfolded": (d.w_uv.numel() + w_o.numel()) * 2, "o_folded": wof.numel() * 2}
+    res = {"workload": name, "path": "projections", "d_model": d_model, "tokens": B * s_q}
+    for k, fn in legs.items():
+        for _ in range(warmup):
+            fl()
+            fn()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            fl()
+            evs[i][0].record(stream)
+            fn()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms = _stats([e[0].elapsed_time(e[1]) for e in evs])[0]
+        res[k] = {"ms": ms, "weight_MB": wbytes[k] / 1e6,
+                  "weight_GBs": wbytes[k] / (ms * 1e-3) / 1e9}
+    return res
+
+
 def time_append(name, steps, warmup, d_model=5120, flush=True):
     """Cache-append step (write side): the step's new tokens projected, rotated and
     written into the paged cache."""
@@ -447,6 +508,11 @@ def main():
         name = args.workload if args.workload.startswith("gqla") else "gqla-b32-t65536"
         print(json.dumps(time_expand(name, args.steps, min(args.warmup, 20),
                                      flush=not args.no_flush)), flush=True)
+        return
+    if args.path == "projections":
+        for name in ("long-b4-t131072", "dsv2-b16-t4096", "mtp-b64-ragged"):
+            print(json.dumps(time_projections(name, args.steps, min(args.warmup, 20),
+                                              flush=not args.no_flush)), flush=True)
         return
     if args.path == "gqa":
         g = time_gqa_path(args.workload, args.steps, args.warmup, flush=not args.no_flush)
@@ -542,6 +608,10 @@ def main():
                   file=sys.stderr, flush=True)
         print(json.dumps(time_expand("gqla-b32-t65536", args.steps, min(args.warmup, 20),
                                      flush=not args.no_flush)), file=sys.stderr, flush=True)
+        for name in ("long-b4-t131072", "dsv2-b16-t4096"):
+            print(json.dumps(time_projections(name, args.steps, min(args.warmup, 20),
+                                              flush=not args.no_flush)), file=sys.stderr,
+                  flush=True)
         for name in ("long-b4-t131072", "mtp-b64-ragged"):
             print(json.dumps(time_append(name, args.steps, args.warmup,
                                          flush=not args.no_flush)),

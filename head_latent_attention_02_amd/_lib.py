@@ -20,7 +20,8 @@ MLA_F32, MLA_BF16 = 0, 1
 # every symbol include/mla.h declares
 EXPORTS = ("mla_absorb_q", "mla_decode_absorbed", "mla_splitkv_combine", "mla_out_uv",
            "gqla_decode_gqa", "gqla_expand_cache", "mla_cache_append", "mla_decode_step",
-           "gqla_decode_step",
+           "gqla_decode_step", "mla_project_q", "mla_fold_q_weights", "mla_project_q_folded",
+           "mla_out_project", "mla_fold_o_weights", "mla_out_project_folded",
            "mla_cache_scalars_per_token", "gqla_cache_scalars_per_token",
            "mla_decode_kernel_kind", "gqla_decode_kernel_kind", "mla_checked_bad_pages",
            "mla_status_str")
@@ -70,6 +71,12 @@ def load(checked=False):
             "mla_cache_append": [S, ctypes.c_int32, ctypes.c_float, P, P, P, P, P, P, P],
             "mla_decode_step": [S, P, P, P, P, P, P, P, P, P, P, P, P, P],
             "gqla_decode_step": [S, P, P, P, P, P, P, P, P, P, P, P],
+            "mla_project_q": [S, ctypes.c_int32, ctypes.c_float, P, P, P, P, P],
+            "mla_fold_q_weights": [S, ctypes.c_int32, P, P, P, P],
+            "mla_project_q_folded": [S, ctypes.c_int32, ctypes.c_float, P, P, P, P, P],
+            "mla_out_project": [S, ctypes.c_int32, P, P, P, P],
+            "mla_fold_o_weights": [S, ctypes.c_int32, P, P, P, P],
+            "mla_out_project_folded": [S, ctypes.c_int32, P, P, P, P],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -202,3 +209,33 @@ def gqla_decode_kernel_kind(shape):
 
 def mla_status_str(status):
     return status_str(status)
+
+
+def mla_project_q(shape, d_model, rope_base, x, w_q, ctx_lens, q, stream=None, check=True):
+    return _call("mla_project_q", shape, (x, w_q, ctx_lens, q), stream, check,
+                 mid=(int(d_model), float(rope_base)))
+
+
+def mla_fold_q_weights(shape, d_model, w_q, w_uk, w_q_folded, stream=None, check=True):
+    return _call("mla_fold_q_weights", shape, (w_q, w_uk, w_q_folded), stream, check,
+                 mid=(int(d_model),))
+
+
+def mla_project_q_folded(shape, d_model, rope_base, x, w_q_folded, ctx_lens, q_abs,
+                         stream=None, check=True):
+    return _call("mla_project_q_folded", shape, (x, w_q_folded, ctx_lens, q_abs), stream,
+                 check, mid=(int(d_model), float(rope_base)))
+
+
+def mla_out_project(shape, d_model, out, w_o, y, stream=None, check=True):
+    return _call("mla_out_project", shape, (out, w_o, y), stream, check, mid=(int(d_model),))
+
+
+def mla_fold_o_weights(shape, d_model, w_o, w_uv, w_o_folded, stream=None, check=True):
+    return _call("mla_fold_o_weights", shape, (w_o, w_uv, w_o_folded), stream, check,
+                 mid=(int(d_model),))
+
+
+def mla_out_project_folded(shape, d_model, o_lat, w_o_folded, y, stream=None, check=True):
+    return _call("mla_out_project_folded", shape, (o_lat, w_o_folded, y), stream, check,
+                 mid=(int(d_model),))

@@ -51,4 +51,16 @@ hipError_t launch_expand_cache_mfma(const mla_shape_t& s, const void* pool, cons
                                     const void* w_uv, void* k, void* v, void* kr,
                                     hipStream_t st);
 
+// the projections around the path, unfolded and folded (bf16 weights)
+bool projections_supported(const mla_shape_t& s, int d_model);
+hipError_t launch_project_q(const mla_shape_t& s, int d_model, float rope_base, const void* x,
+                            const void* w, const int32_t* lens, void* q, bool folded,
+                            hipStream_t st);
+hipError_t launch_out_project(const mla_shape_t& s, int d_model, const float* in,
+                              const void* w, float* y, bool folded, hipStream_t st);
+hipError_t launch_fold_q(const mla_shape_t& s, int d_model, const void* w_q, const void* w_uk,
+                         void* w_qf, hipStream_t st);
+hipError_t launch_fold_o(const mla_shape_t& s, int d_model, const void* w_o, const void* w_uv,
+                         void* w_of, hipStream_t st);
+
 }  // namespace mla

@@ -193,6 +193,70 @@ mla_status_t mla_cache_append(const mla_shape_t* s, int32_t d_model, float rope_
                                              page_table, ctx_lens, kv_pool, stream));
 }
 
+// The projections around the path (offline absorption): shared argument checks.
+static mla_status_t validate_proj(const mla_shape_t* s, int32_t d_model) {
+  mla_status_t v = validate(s);
+  if (v != MLA_OK) return v;
+  if (d_model <= 0) return MLA_ERR_SHAPE;
+  if (!mla::projections_supported(*s, d_model)) return MLA_ERR_UNSUPPORTED;
+  if ((static_cast<int64_t>(s->batch) * s->s_q + 31) / 32 > 65535) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+mla_status_t mla_project_q(const mla_shape_t* s, int32_t d_model, float rope_base,
+                           const void* x, const void* w_q, const int32_t* ctx_lens, void* q,
+                           hipStream_t stream) {
+  mla_status_t v = validate_proj(s, d_model);
+  if (v != MLA_OK) return v;
+  if (!x || !w_q || !ctx_lens || !q) return MLA_ERR_NULL;
+  if (!(rope_base > 0.f) || !isfinite(rope_base)) return MLA_ERR_SHAPE;
+  return hip_status(mla::launch_project_q(*s, d_model, rope_base, x, w_q, ctx_lens, q, false,
+                                          stream));
+}
+
+mla_status_t mla_fold_q_weights(const mla_shape_t* s, int32_t d_model, const void* w_q,
+                                const void* w_uk, void* w_q_folded, hipStream_t stream) {
+  mla_status_t v = validate_proj(s, d_model);
+  if (v != MLA_OK) return v;
+  if (!w_q || !w_uk || !w_q_folded) return MLA_ERR_NULL;
+  return hip_status(mla::launch_fold_q(*s, d_model, w_q, w_uk, w_q_folded, stream));
+}
+
+mla_status_t mla_project_q_folded(const mla_shape_t* s, int32_t d_model, float rope_base,
+                                  const void* x, const void* w_q_folded,
+                                  const int32_t* ctx_lens, void* q_abs, hipStream_t stream) {
+  mla_status_t v = validate_proj(s, d_model);
+  if (v != MLA_OK) return v;
+  if (!x || !w_q_folded || !ctx_lens || !q_abs) return MLA_ERR_NULL;
+  if (!(rope_base > 0.f) || !isfinite(rope_base)) return MLA_ERR_SHAPE;
+  return hip_status(mla::launch_project_q(*s, d_model, rope_base, x, w_q_folded, ctx_lens,
+                                          q_abs, true, stream));
+}
+
+mla_status_t mla_out_project(const mla_shape_t* s, int32_t d_model, const float* out,
+                             const void* w_o, float* y, hipStream_t stream) {
+  mla_status_t v = validate_proj(s, d_model);
+  if (v != MLA_OK) return v;
+  if (!out || !w_o || !y) return MLA_ERR_NULL;
+  return hip_status(mla::launch_out_project(*s, d_model, out, w_o, y, false, stream));
+}
+
+mla_status_t mla_fold_o_weights(const mla_shape_t* s, int32_t d_model, const void* w_o,
+                                const void* w_uv, void* w_o_folded, hipStream_t stream) {
+  mla_status_t v = validate_proj(s, d_model);
+  if (v != MLA_OK) return v;
+  if (!w_o || !w_uv || !w_o_folded) return MLA_ERR_NULL;
+  return hip_status(mla::launch_fold_o(*s, d_model, w_o, w_uv, w_o_folded, stream));
+}
+
+mla_status_t mla_out_project_folded(const mla_shape_t* s, int32_t d_model, const float* o_lat,
+                                    const void* w_o_folded, float* y, hipStream_t stream) {
+  mla_status_t v = validate_proj(s, d_model);
+  if (v != MLA_OK) return v;
+  if (!o_lat || !w_o_folded || !y) return MLA_ERR_NULL;
+  return hip_status(mla::launch_out_project(*s, d_model, o_lat, w_o_folded, y, true, stream));
+}
+
 mla_status_t mla_decode_step(const mla_shape_t* s, const void* q, const void* w_uk,
                              const void* w_uv, const void* kv_pool, const int32_t* page_table,
                              const int32_t* ctx_lens, void* q_abs, float* o_part,

@@ -166,6 +166,50 @@ mla_status_t mla_cache_append(const mla_shape_t* shape, int32_t d_model, float r
                               const int32_t* page_table, const int32_t* ctx_lens,
                               void* kv_pool, hipStream_t stream);
 
+/* Projections around the path, unfolded and folded offline ("How to upgrade GQA models to
+ * MLA...", Under the hood, Decompression Multiplex: by associativity W_UK is multiplied into
+ * the query weights W^Q ahead of time, so the query lands in the latent space directly; the
+ * value side folds W_UV into the output projection W^O the same way, which the pages do not
+ * name).  All six need dtype MLA_BF16 (weights and x bf16), d_model a multiple of 256,
+ * H * (d_nope + d_rope), H * (d_c + d_rope) and d_model multiples of 64, H * d_v and H * d_c
+ * multiples of 256 and d_rope even (else MLA_ERR_UNSUPPORTED); fp32 accumulate.
+ *   x     [B, s_q, d_model]                 hidden states of the new tokens (bf16)
+ *   w_q   [H, d_nope + d_rope, d_model]     query weights, no-position rows first
+ *   w_o   [d_model, H * d_v]                output projection
+ * The query's RoPE rows are rotated at the token's position t = ctx_lens[b] - s_q + s with
+ * the cache key's rotation (pairs (2i, 2i+1) turned by t * rope_base^(-2i / d_rope)).
+ *
+ * mla_project_q:        q[b,s,h] = [W^Q_nope[h] x ; RoPE_t(W^Q_rope[h] x)]  -> q [B,s_q,H,d_nope+d_rope]
+ *                       bf16, the input of mla_absorb_q.
+ * mla_fold_q_weights:   w_q_folded[h] = [W_UK[w(h)]^T W^Q_nope[h] ; W^Q_rope[h]]
+ *                       [H, d_c + d_rope, d_model] bf16 (set-up, once per weight set).
+ * mla_project_q_folded: q_abs[b,s,h] = [w_q_folded_lat[h] x ; RoPE_t(W^Q_rope[h] x)]
+ *                       -> q_abs [B,s_q,H,d_c+d_rope] bf16, the input of mla_decode_absorbed
+ *                       (no mla_absorb_q).
+ * mla_out_project:      y[b,s] = W^O out[b,s] (out [B,s_q,H,d_v] fp32 from mla_out_uv)
+ *                       -> y [B,s_q,d_model] fp32.
+ * mla_fold_o_weights:   w_o_folded[:, h d_c + c] = sum_i W^O[:, h d_v + i] W_UV[w(h)][i][c]
+ *                       [d_model, H * d_c] bf16 (set-up).
+ * mla_out_project_folded: y[b,s] = w_o_folded o_lat[b,s] (o_lat [B,s_q,H,d_c] fp32 from
+ *                       mla_splitkv_combine) -> y fp32 (no mla_out_uv).
+ * y is accumulated with atomic adds over K ranges when d_model alone gives few workgroups,
+ * so its last bits may differ between calls. */
+mla_status_t mla_project_q(const mla_shape_t* shape, int32_t d_model, float rope_base,
+                           const void* x, const void* w_q, const int32_t* ctx_lens, void* q,
+                           hipStream_t stream);
+mla_status_t mla_fold_q_weights(const mla_shape_t* shape, int32_t d_model, const void* w_q,
+                                const void* w_uk, void* w_q_folded, hipStream_t stream);
+mla_status_t mla_project_q_folded(const mla_shape_t* shape, int32_t d_model, float rope_base,
+                                  const void* x, const void* w_q_folded,
+                                  const int32_t* ctx_lens, void* q_abs, hipStream_t stream);
+mla_status_t mla_out_project(const mla_shape_t* shape, int32_t d_model, const float* out,
+                             const void* w_o, float* y, hipStream_t stream);
+mla_status_t mla_fold_o_weights(const mla_shape_t* shape, int32_t d_model, const void* w_o,
+                                const void* w_uv, void* w_o_folded, hipStream_t stream);
+mla_status_t mla_out_project_folded(const mla_shape_t* shape, int32_t d_model,
+                                    const float* o_lat, const void* w_o_folded, float* y,
+                                    hipStream_t stream);
+
 /* Whole absorbed step a1 -> a2 -> a3 -> a4 on one stream.  The caller provides the
  * workspaces: q_abs [B,s_q,H,D] dtype, o_part [B,s_q,H,S,d_c] fp32,
  * lse_part [B,s_q,H,S] fp32, o_lat [B,s_q,H,d_c] fp32.  out [B,s_q,H,d_v] fp32,

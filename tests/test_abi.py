@@ -160,6 +160,27 @@ def test_error_raises_with_check():
         mla.mla_absorb_q(good_shape(batch=0), 1, 1, 1, stream=0)
 
 
+def test_projection_arguments_checked():
+    s = good_shape(d_c=512, d_rope=64, d_nope=128, d_v=128, n_heads=128, n_wheads=128,
+                   dtype="bf16")
+    fake = 0x1000
+    assert mla.mla_project_q(s, 5120, 1e4, fake, fake, fake, None, stream=0,
+                             check=False) == mla.MLA_ERR_NULL
+    assert mla.mla_project_q(s, 5000, 1e4, fake, fake, fake, fake, stream=0,
+                             check=False) == mla.MLA_ERR_UNSUPPORTED   # d_model % 256
+    assert mla.mla_project_q(s, 0, 1e4, fake, fake, fake, fake, stream=0,
+                             check=False) == mla.MLA_ERR_SHAPE
+    assert mla.mla_project_q(s, 5120, -1.0, fake, fake, fake, fake, stream=0,
+                             check=False) == mla.MLA_ERR_SHAPE
+    f32 = good_shape(d_c=512, d_rope=64, d_nope=128, d_v=128, n_heads=128, n_wheads=128)
+    for fn, args in ((mla.mla_fold_q_weights, (fake, fake, fake)),
+                     (mla.mla_out_project, (fake, fake, fake)),
+                     (mla.mla_fold_o_weights, (fake, fake, fake)),
+                     (mla.mla_out_project_folded, (fake, fake, fake))):
+        assert fn(f32, 5120, *args, stream=0, check=False) == mla.MLA_ERR_UNSUPPORTED
+        assert fn(s, 5120, fake, fake, None, stream=0, check=False) == mla.MLA_ERR_NULL
+
+
 def test_kernel_kind_is_host_only():
     assert mla.mla_decode_kernel_kind(good_shape()) in (0, 1)
     assert mla.gqla_decode_kernel_kind(good_shape(n_wheads=2)) in (0, 1)
