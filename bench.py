@@ -66,7 +66,8 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--extra", action="store_true",
                     help="also time the other workloads (stderr lines)")
-    ap.add_argument("--path", choices=("absorbed", "gqa", "expand", "projections"),
+    ap.add_argument("--path", choices=("absorbed", "gqa", "expand", "projections",
+                                       "moving-reference"),
                     default="absorbed",
                     help="absorbed MLA step (default), the GQLA per-group GQA path, or the "
                          "GQA path's cache expansion alone (a stderr-style JSON line)")
@@ -346,6 +347,54 @@ def time_gqa_path(name, steps, warmup, flush=True):
             "kernel": "mfma" if mla.gqla_decode_kernel_kind(sh) == 1 else "generic"}
 
 
+def time_moving_reference(name, steps, warmup, flush=True):
+    """The decode kernel's worst case: scores that climb on every tile of every chunk, so
+    every row's softmax reference moves on every tile (workloads.gen.growing_score_inputs),
+    timed beside the same kernel on the benign seeded workload."""
+    import torch
+    import head_latent_attention_02_amd as mla
+    from workloads import get_config, make_inputs
+    from workloads.device import DeviceInputs
+    from workloads.gen import growing_score_inputs
+
+    cfg = get_config(name)
+    res = {"workload": name, "path": "absorbed decode, reference moving on every tile"}
+    stream = torch.cuda.current_stream()
+    fl = _flusher() if flush else (lambda: None)
+    T = None
+    for kind in ("benign", "moving"):
+        if kind == "benign":
+            inp = make_inputs(cfg)
+        else:
+            per_split = -(-T // cfg.n_splits)                     # ceil(T / S)
+            chunk = -(-per_split // cfg.page_size) * cfg.page_size  # page-aligned chunk
+            inp = growing_score_inputs(cfg, period_tokens=chunk)
+        T = int(inp.ctx_lens[0])
+        d = DeviceInputs(inp)
+        op = d.o_part_view(cfg.d_c)
+        mla.mla_absorb_q(d.shape, d.q, d.w_uk, d.q_abs)
+
+        def run():
+            mla.mla_decode_absorbed(d.shape, d.q_abs, d.pool, d.page_table, d.ctx_lens, op,
+                                    d.lse_part, stream=stream.cuda_stream)
+        for _ in range(warmup):
+            fl()
+            run()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            fl()
+            evs[i][0].record(stream)
+            run()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        res[kind + "_decode_ms"] = _stats([e[0].elapsed_time(e[1]) for e in evs])[0]
+        del d
+        torch.cuda.empty_cache()
+    res["ratio"] = res["moving_decode_ms"] / res["benign_decode_ms"]
+    return res
+
+
 def time_expand(name, steps, warmup, flush=True):
     """a6, the GQA path's set-up: the per-group K, V and shared RoPE-key cache built from the
     latent cache (every pool row, padding included), timed alone with events around it."""
@@ -509,6 +558,11 @@ def main():
         print(json.dumps(time_expand(name, args.steps, min(args.warmup, 20),
                                      flush=not args.no_flush)), flush=True)
         return
+    if args.path == "moving-reference":
+        for name in ("long-b4-t131072", "gqla-b32-t8192"):
+            print(json.dumps(time_moving_reference(name, args.steps, min(args.warmup, 200),
+                                                   flush=not args.no_flush)), flush=True)
+        return
     if args.path == "projections":
         for name in ("long-b4-t131072", "dsv2-b16-t4096", "mtp-b64-ragged"):
             print(json.dumps(time_projections(name, args.steps, min(args.warmup, 20),
@@ -608,6 +662,10 @@ def main():
                   file=sys.stderr, flush=True)
         print(json.dumps(time_expand("gqla-b32-t65536", args.steps, min(args.warmup, 20),
                                      flush=not args.no_flush)), file=sys.stderr, flush=True)
+        for name in ("long-b4-t131072", "gqla-b32-t8192"):
+            print(json.dumps(time_moving_reference(name, args.steps, min(args.warmup, 200),
+                                                   flush=not args.no_flush)),
+                  file=sys.stderr, flush=True)
         for name in ("long-b4-t131072", "dsv2-b16-t4096"):
             print(json.dumps(time_projections(name, args.steps, min(args.warmup, 20),
                                               flush=not args.no_flush)), file=sys.stderr,

@@ -27,10 +27,12 @@
 //  * The score waves (32 rows each, q_abs held in registers as the B operand) issue the 36
 //    MFMAs of tile s and, between them, the softmax of tile s-1 in small pieces that issue
 //    while the matrix core is busy; P (bf16) goes to LDS for the value waves.
-//  * The softmax keeps a lazy per-row reference: it only moves when a score exceeds it by
-//    more than a slack of 32 (log2 units), so P stays below 2^32 and the accumulators
-//    never need rescaling; when a reference must move, the chunk is rerun from its first
-//    tile with the raised reference (rare: each rerun strictly raises a reference).
+//  * The softmax keeps a lazy per-row reference: it only moves when a tile's maximum exceeds
+//    it by more than a slack of 32 (log2 units), so P stays below 2^32.  When it moves, the
+//    score wave rescales the row's running sum by 2^(old - new) and publishes that factor
+//    with P; the value waves rescale the row's accumulators by it before adding the tile.
+//    Every chunk is one pass over its tiles whatever the scores do (a move costs the value
+//    waves one multiply per accumulator).
 //  * The row blocks of one (b, u) are 8 workgroups apart in the grid so that they run on
 //    the same XCD and share its L2.
 #include <math.h>
@@ -91,19 +93,14 @@ struct Smem {
   char ring[kNB][kTileB];
   bf16_t pbuf[2][64 * kPRow];
   float lfin[64];
-  long long flag[2];   // rerun requests: tag of (pass, tile) of the tile that asked
+  float alpha[2][64];  // [tile & 1][row]: factor the accumulators take before that tile
+  int moved[2][2];     // [tile & 1][score wave]: some row of the wave moved its reference
   uint32_t plan[2][kLoads / 2][64];   // value wave VW's per-lane load offsets
 };
 
-// The softmax of tile k runs in slot k+1; a score wave that must move a reference there
-// writes tag(pass, k) into flag[k & 1] during slot k+1.  Every wave reads that word at the
-// start of slot k+2 (after the barrier ending slot k+1), when it is stable (its next write
-// is in slot k+3), and acts on it at the end of the two-slot turn holding slot k+2, so all
-// waves agree without extra barriers; tags of an abandoned pass never match the next one.
-// The request is honoured one or two slots late, which only wastes those slots' work.
-__device__ __forceinline__ long long rerun_tag(int pass, int k) {
-  return (static_cast<long long>(pass) << 32) | static_cast<unsigned>(k);
-}
+// The softmax of tile k runs in slot k+1 and writes alpha[k & 1] and moved[k & 1] there; the
+// value waves read them in slot k+2 (after the barrier ending slot k+1), before multiplying
+// tile k, and the next write of that parity is in slot k+3.
 
 // One wave's share of a tile, in registers between its global loads and its LDS stores.
 template <int NL>
@@ -196,7 +193,7 @@ __device__ __forceinline__ void score_slot(const char* tb, const bf16x8 (&qreg)[
                                            const int (&rb)[4], f32x16& sacc_out,
                                            const f32x16& sacc_in, int lim, float zscale,
                                            float slack, float& m_ref, float& l_run,
-                                           bool& move, bf16_t* prow, int g) {
+                                           bool& move, float& alpha, bf16_t* prow, int g) {
   // A operands run kPF K-steps ahead of the MFMA that consumes them
   constexpr int kPF = SPF;
   bf16x8 abuf[kPF];
@@ -236,11 +233,13 @@ __device__ __forceinline__ void score_slot(const char* tb, const bf16x8 (&qreg)[
         mx4[0] = xhalf_max(mx * zscale);
       } else if (ks == 9) {
         // The first visible tile of a row fixes its reference; a later jump past the
-        // slack raises it to this tile's maximum and asks for a rerun, so a rerun can
-        // never trigger twice on the same tile: every rerun raises some reference.
+        // slack raises it to this tile's maximum, and what was summed so far is rescaled
+        // to the new reference (here the running sum, in the value waves the accumulators).
         const float mt = mx4[0];
         move = m_ref != -INFINITY && mt > m_ref + slack;
+        alpha = move ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.f;
         if (m_ref == -INFINITY || move) m_ref = mt;
+        l_run *= alpha;
         live = m_ref != -INFINITY;
         nm = -m_ref;
       } else if (ks < 18) {               // two probabilities per step, bf16 pairs
@@ -286,52 +285,44 @@ __device__ __forceinline__ void score_wave(Smem& sm, const Work& w, int lane) {
   for (int b4 = 0; b4 < 4; ++b4) rb[b4] = n32 * kRowB + 16 * ((2 * b4 + g) ^ sw);
   const int n = w.n_tiles;
   float m_ref = -INFINITY, l_run = 0.f;
-  int reruns = 0;   // each rerun passes its triggering tile, so at most n_tiles happen
   f32x16 sacc[2];
-  bool restarted = false;
   // one slot; P = parity of s (sacc[P] takes tile s, sacc[1 - P] holds tile s-1).
-  // Slots run in turns of two (even, odd) and every wave acts on a rerun request or the
-  // end of the pass only at the end of a turn, so the value waves' loop has a single
-  // exit; a turn may run one slot past n + 1, which does no work.
-  // Returns true when the pass is over (at an odd slot: last slot done, or a rerun).
+  // Slots run in turns of two (even, odd) and every wave leaves the loop only at the end of
+  // a turn, so the value waves' loop has a single exit; a turn may run one slot past n + 1,
+  // which does no work.  Returns true when the pass is over (at an odd slot).
   auto slot = [&](auto par, int s) -> bool {
     constexpr int P = decltype(par)::value;
-    const long long seen = (s >= 2) ? sm.flag[s & 1] : -1;   // tile s-2's request
     const bool mf = s < n, sf = s >= 1 && s <= n;
     const char* tb = &sm.ring[s & (kNB - 1)][0];
     const int lim = top_row - (w.lo + (s - 1) * kTT);
     bf16_t* prow = &sm.pbuf[(s - 1) & 1][(32 * QW + n32) * kPRow];
     bool move = false;
+    float alpha = 1.f;
     const bool masked = __builtin_amdgcn_ballot_w64(lim < kTT) != 0;
     if (mf && sf && !masked)
       score_slot<true, true, false, SPF>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
-                                    w.slack, m_ref, l_run, move, prow, g);
+                                    w.slack, m_ref, l_run, move, alpha, prow, g);
     else if (mf && sf)
       score_slot<true, true, true, SPF>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
-                                   w.slack, m_ref, l_run, move, prow, g);
+                                   w.slack, m_ref, l_run, move, alpha, prow, g);
     else if (mf)
       score_slot<true, false, false, SPF>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
-                                     w.slack, m_ref, l_run, move, prow, g);
+                                     w.slack, m_ref, l_run, move, alpha, prow, g);
     else if (sf)
       score_slot<false, true, true, SPF>(tb, qreg, rb, sacc[P], sacc[1 - P], lim, w.zscale,
-                                    w.slack, m_ref, l_run, move, prow, g);
-    if (sf && __builtin_amdgcn_ballot_w64(move) && reruns <= n)
-      sm.flag[(s - 1) & 1] = rerun_tag(reruns, s - 1);
-    const bool rerun = s >= 2 && seen == rerun_tag(reruns, s - 2);
-    __syncthreads();
-    if (rerun) restarted = true;
-    return P == 1 && (restarted || s >= n + 1);
-  };
-  while (true) {
-    l_run = 0.f;
-    restarted = false;
-    __syncthreads();   // the value waves have stored tile 0
-    for (int s = 0;; s += 2) {
-      slot(std::integral_constant<int, 0>(), s);
-      if (slot(std::integral_constant<int, 1>(), s + 1)) break;
+                                    w.slack, m_ref, l_run, move, alpha, prow, g);
+    if (sf) {   // tile s-1's rescale factors, for the value waves in slot s+1
+      if (g == 0) sm.alpha[(s - 1) & 1][32 * QW + n32] = alpha;
+      const bool any = __builtin_amdgcn_ballot_w64(move) != 0;
+      if (n32 == 0 && g == 0) sm.moved[(s - 1) & 1][QW] = any ? 1 : 0;
     }
-    if (!restarted) break;
-    ++reruns;
+    __syncthreads();
+    return P == 1 && s >= n + 1;
+  };
+  __syncthreads();   // the streaming waves have stored tile 0
+  for (int s = 0;; s += 2) {
+    slot(std::integral_constant<int, 0>(), s);
+    if (slot(std::integral_constant<int, 1>(), s + 1)) break;
   }
   const float l_tot = xhalf_sum(l_run);
   if (g == 0) {
@@ -407,6 +398,24 @@ __device__ __forceinline__ void value_ring_tile(Smem& sm, int slot, int pb_i,
   }
 }
 
+// Before the value waves add tile k: if some row's reference moved in tile k, every row's
+// accumulators take that row's factor (1 for rows that did not move).  Lane (n32, g) holds
+// rows 32 nb + n32 of the block.
+template <int KMB, int NQ>
+__device__ __forceinline__ void rescale_if_moved(Smem& sm, int k, int n32,
+                                                 f32x16 (&acc)[KMB][NQ]) {
+  int any = sm.moved[k & 1][0];
+  if (NQ > 1) any |= sm.moved[k & 1][1];
+  if (__builtin_amdgcn_readfirstlane(any)) {
+#pragma unroll
+    for (int nb = 0; nb < NQ; ++nb) {
+      const float a = sm.alpha[k & 1][32 * nb + n32];
+#pragma unroll
+      for (int mb = 0; mb < KMB; ++mb) acc[mb][nb] *= a;
+    }
+  }
+}
+
 // Value wave VW of the 32-row layout: latent columns [256 VW, 256 VW + 256) of the block's
 // rows (32 NQ).  It also streams half of every tile through the ring (below) and, in slot s,
 // multiplies tile s-2.
@@ -436,8 +445,7 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
   Stage<kLoads> stg[2];
   uint32_t (&plan)[kLoads / 2][64] = sm.plan[VW];
   make_plan(plan, lane, VW);
-  int reruns = 0;
-  while (true) {
+  {
     // Loads and stores are unconditional: past the last tile they repeat tile n-1 into
     // ring slot (s+1) % 4, which no wave reads in slot s and no later slot needs.
     const int last = max(n - 1, 0);
@@ -469,41 +477,33 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
     // slot s stores tile s+1 from stg[(s+1) & 1], reloads that buffer with tile s+3 and
     // multiplies tile s-2 (none past the last tile: a turn can run one slot past n+1)
     f32x16 acc[8][NQ];
-    long long seen;
-    bool restarted = false;
     auto vslot = [&](auto par, int s) {
       constexpr int X = decltype(par)::value;   // (s + 1) & 1
-      seen = sm.flag[s & 1];
       store_stage(sm, stg[X], lane, s + 1, VW, 2);
       __builtin_amdgcn_sched_barrier(0);
       load_stage(stg[X], plan, w, min(s + 3, last), lane);
       __builtin_amdgcn_sched_barrier(0);
-      if (s - 2 < n)
+      if (s - 2 < n) {
+        rescale_if_moved<8, NQ>(sm, s - 2, n32, acc);
         value_ring_tile<NQ, false>(sm, (s - 2) & (kNB - 1), (s - 2) & 1, trofs, n32, g, acc);
-      restarted |= seen == rerun_tag(reruns, s - 2);
+      }
       __syncthreads();
     };
     // turn (2, 3); slot 2 is peeled so the accumulators are first written outside the loop
-    seen = sm.flag[0];
     store_stage(sm, stg[1], lane, 3, VW, 2);
     __builtin_amdgcn_sched_barrier(0);
     load_stage(stg[1], plan, w, min(5, last), lane);
     __builtin_amdgcn_sched_barrier(0);
     value_ring_tile<NQ, true>(sm, 0, 0, trofs, n32, g, acc);
-    restarted = seen == rerun_tag(reruns, 0);
     __syncthreads();
     vslot(std::integral_constant<int, 0>(), 3);
     // turns (4, 5), (6, 7), ...: the pass ends after the turn holding slot n + 1
-    if (!restarted && n + 1 > 3) {
+    if (n + 1 > 3) {
       for (int s = 4;; s += 2) {
         vslot(std::integral_constant<int, 1>(), s);
         vslot(std::integral_constant<int, 0>(), s + 1);
-        if (restarted || s + 1 >= n + 1) break;
+        if (s + 1 >= n + 1) break;
       }
-    }
-    if (restarted) {
-      ++reruns;
-      continue;
     }
     __syncthreads();   // the score waves have published the row sums
 #pragma unroll
@@ -540,8 +540,7 @@ __device__ __forceinline__ void loader_wave(Smem& sm, const Work& w, int lane) {
   Stage<kLoads> stg[2];
   uint32_t (&plan)[kLoads / 2][64] = sm.plan[LW];
   make_plan(plan, lane, LW);
-  int reruns = 0;
-  while (true) {
+  {
     const int last = max(n - 1, 0);
     load_stage(stg[0], plan, w, 0, lane);
     load_stage(stg[1], plan, w, min(1, last), lane);
@@ -561,34 +560,24 @@ __device__ __forceinline__ void loader_wave(Smem& sm, const Work& w, int lane) {
       __syncthreads();
       return;
     }
-    long long seen;
-    bool restarted = false;
     auto lslot = [&](auto par, int s) {
       constexpr int X = decltype(par)::value;
-      seen = sm.flag[s & 1];
       store_stage(sm, stg[X], lane, s + 1, LW, 2);
       __builtin_amdgcn_sched_barrier(0);
       load_stage(stg[X], plan, w, min(s + 3, last), lane);
-      restarted |= seen == rerun_tag(reruns, s - 2);
       __syncthreads();
     };
-    seen = sm.flag[0];
     store_stage(sm, stg[1], lane, 3, LW, 2);
     __builtin_amdgcn_sched_barrier(0);
     load_stage(stg[1], plan, w, min(5, last), lane);
-    restarted = seen == rerun_tag(reruns, 0);
     __syncthreads();
     lslot(std::integral_constant<int, 0>(), 3);
-    if (!restarted && n + 1 > 3) {
+    if (n + 1 > 3) {
       for (int s = 4;; s += 2) {
         lslot(std::integral_constant<int, 1>(), s);
         lslot(std::integral_constant<int, 0>(), s + 1);
-        if (restarted || s + 1 >= n + 1) break;
+        if (s + 1 >= n + 1) break;
       }
-    }
-    if (restarted) {
-      ++reruns;
-      continue;
     }
     __syncthreads();
     return;
@@ -616,8 +605,7 @@ __device__ __forceinline__ void value_wave128(Smem& sm, const Work& w, int lane)
         trofs[par][kt][h4] = tok * kRowB + (((col >> 3) ^ rswz(tok)) * 16) + (col & 7) * 2;
       }
   const int n = w.n_tiles;
-  int reruns = 0;
-  while (true) {
+  {
     __syncthreads();
     __syncthreads();
     __syncthreads();
@@ -631,31 +619,23 @@ __device__ __forceinline__ void value_wave128(Smem& sm, const Work& w, int lane)
       return;
     }
     f32x16 acc[KMB][NQ];
-    long long seen;
-    bool restarted = false;
     auto vslot = [&](int s) {
-      seen = sm.flag[s & 1];
-      if (s - 2 < n)
+      if (s - 2 < n) {
+        rescale_if_moved<KMB, NQ>(sm, s - 2, n32, acc);
         value_ring_tile<NQ, false, KMB>(sm, (s - 2) & (kNB - 1), (s - 2) & 1, trofs, n32, g,
                                         acc);
-      restarted |= seen == rerun_tag(reruns, s - 2);
+      }
       __syncthreads();
     };
-    seen = sm.flag[0];
     value_ring_tile<NQ, true, KMB>(sm, 0, 0, trofs, n32, g, acc);
-    restarted = seen == rerun_tag(reruns, 0);
     __syncthreads();
     vslot(3);
-    if (!restarted && n + 1 > 3) {
+    if (n + 1 > 3) {
       for (int s = 4;; s += 2) {
         vslot(s);
         vslot(s + 1);
-        if (restarted || s + 1 >= n + 1) break;
+        if (s + 1 >= n + 1) break;
       }
-    }
-    if (restarted) {
-      ++reruns;
-      continue;
     }
     __syncthreads();
 #pragma unroll
@@ -730,7 +710,6 @@ void decode_absorbed_mfma_r32_kernel(
   __shared__ __attribute__((aligned(16))) ring::Smem sm;
   MLA_SETUP_WORK(NQ)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (threadIdx.x == 0) sm.flag[0] = sm.flag[1] = -1;
   __syncthreads();
   if (wave == 0)
     ring::score_wave<NQ, 0>(sm, w, lane);
@@ -755,7 +734,6 @@ __global__ __launch_bounds__(512, 1) void decode_absorbed_mfma_r64_kernel(
   __shared__ __attribute__((aligned(16))) ring::Smem sm;
   MLA_SETUP_WORK(NQ)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (threadIdx.x == 0) sm.flag[0] = sm.flag[1] = -1;
   __syncthreads();
   switch (wave) {
     case 0: ring::score_wave<NQ, 0, 4>(sm, w, lane); break;
@@ -789,7 +767,7 @@ hipError_t launch_decode_absorbed_mfma(const mla_shape_t& s, const void* q_abs,
   const unsigned grid = static_cast<unsigned>((n_units + 7) / 8) * 8u * n_yblk;
   const float zscale = s.softmax_scale * kLog2e;
   // Slack (log2 units) before a row's reference maximum moves; the default keeps P below
-  // 2^32.  MLA_DECODE_REF_SLACK (0..64) overrides it, e.g. 0 to exercise the rerun path.
+  // 2^32.  MLA_DECODE_REF_SLACK (0..64) overrides it, e.g. 0 to exercise the rescale path.
   float slack = 32.f;
   if (const char* e = getenv("MLA_DECODE_REF_SLACK")) {
     const float v = strtof(e, nullptr);

@@ -492,9 +492,10 @@ def test_full_gqla_b32_t65536_gqa_path(name):
 # ------------------------------------------- reference moves (online-softmax rerun path)
 
 @pytest.mark.parametrize("slack", ["0", "0.25"])
-def test_reference_moves_rerun_path(slack, monkeypatch):
+def test_reference_moves_rescale_path(slack, monkeypatch):
     """With no slack the per-row reference moves whenever a tile raises the maximum, so
-    the matrix-core kernel reruns chunks many times; the result must not change."""
+    the matrix-core kernel rescales running sums and accumulators many times; the result
+    must not change."""
     monkeypatch.setenv("MLA_DECODE_REF_SLACK", slack)
     cfg = small(batch=3, s_q=2, ctx=("list", [1500, 700, 65]))
     errs = check_absorbed_all_steps(make_inputs(cfg, seed=12), S=3)
@@ -502,9 +503,9 @@ def test_reference_moves_rerun_path(slack, monkeypatch):
 
 
 @pytest.mark.parametrize("slack", ["0", "0.25"])
-def test_reference_moves_rerun_path_32_row_blocks(slack, monkeypatch):
-    """The rerun path of the 32-row-block kernel (GQLA's absorbed shape, 32 heads): with no
-    slack every raised maximum reruns the chunk; the result must not change."""
+def test_reference_moves_rescale_path_32_row_blocks(slack, monkeypatch):
+    """The rescale path of the 32-row-block kernel (GQLA's absorbed shape, 32 heads): with no
+    slack every raised maximum rescales; the result must not change."""
     monkeypatch.setenv("MLA_DECODE_REF_SLACK", slack)
     cfg = small("gqla-b32-t8192", batch=3, s_q=1, ctx=("list", [1500, 700, 65]))
     assert cfg.s_q * cfg.n_heads == 32          # one block of 32 query rows per sequence
@@ -515,17 +516,19 @@ def test_reference_moves_rerun_path_32_row_blocks(slack, monkeypatch):
 def test_growing_scores_move_the_reference_by_large_steps():
     """Scores that climb by ~38 log2 units per tile move the reference at the default
     slack on every tile; the result must still match the oracle."""
+    from workloads.gen import growing_score_inputs
     cfg = small(batch=2, ctx=("list", [2000, 900]), n_splits=3)
-    inp = make_inputs(cfg, seed=13)
-    inp.q[...] = 0.0
-    inp.q[..., cfg.d_nope] = 40.0                       # only the first RoPE coordinate
-    pool = inp.pool_f32().copy()
-    for b in range(cfg.batch):
-        for i, p in enumerate(inp.page_table[b]):
-            if p < 0:
-                continue
-            t = i * cfg.page_size + np.arange(cfg.page_size)
-            pool[p, :, cfg.d_c] = (t // 32) * 16.0        # exact in bf16
-    from workloads.gen import bf16_bits
-    inp.pool = bf16_bits(pool)
-    check_absorbed_all_steps(inp)
+    check_absorbed_all_steps(growing_score_inputs(cfg, period_tokens=1 << 20, seed=13))
+
+
+@pytest.mark.parametrize("name", ["long-b4-t131072", "gqla-b32-t8192"])
+def test_growing_scores_full_chunks(name):
+    """A reference move on every tile of every chunk (scores restart their climb at each
+    chunk start), for both ring kernels, on shortened contexts; against the oracle."""
+    from workloads.gen import growing_score_inputs
+    kw = dict(batch=2, ctx=("list", [8192, 5000])) if name.startswith("long") else \
+        dict(batch=2, ctx=("list", [4096, 1000]))
+    cfg = small(name, **kw)
+    check_absorbed_all_steps(growing_score_inputs(cfg, period_tokens=8192 // cfg.n_splits
+                                                  if name.startswith("long") else 4096 // 8,
+                                                  seed=15))

@@ -215,3 +215,26 @@ def make_projection_inputs(cfg: Config, d_model=5120, seed=None):
     if bf16:
         w_q, w_o = bf16_round(w_q), bf16_round(w_o)
     return ProjectionInputs(x, w_q, w_o)
+
+
+def growing_score_inputs(cfg: Config, period_tokens, q_value=40.0, step=16.0, seed=None):
+    """A workload whose scores climb on every 32-token tile (the rows' softmax reference must
+    move on each one): q is zero except its first RoPE coordinate (q_value), and the first
+    RoPE coordinate of the cached token at logical position t is step * ((t % period) // 32).
+    With q_value 40, step 16 and the 1/sqrt(576) scale the score rises by 26.7 nats (38.5 log2
+    units) per tile and restarts every ``period_tokens`` tokens (one split chunk).  The values
+    are exact in bf16 while (period / 32 - 1) < 256."""
+    inp = make_inputs(cfg, seed=seed)
+    inp.q[...] = 0.0
+    inp.q[..., cfg.d_nope] = q_value
+    pool = inp.pool_f32().copy()
+    for b in range(cfg.batch):
+        T = int(inp.ctx_lens[b])
+        for i in range(-(-T // cfg.page_size)):
+            page = inp.page_table[b, i]
+            t = i * cfg.page_size + np.arange(cfg.page_size)
+            vals = (((t % period_tokens) // 32) * step).astype(np.float32)
+            live = t < T
+            pool[page, live, cfg.d_c] = vals[live]
+    inp.pool = bf16_bits(pool) if cfg.dtype == "bf16" else pool
+    return inp
