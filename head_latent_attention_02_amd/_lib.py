@@ -14,13 +14,15 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 # the same library built with MLA_CHECKED: page-table entries bounds-checked on the device
 CHECKED_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_checked.so")
 
-MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = range(5)
+MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP, MLA_ERR_TOO_LARGE = range(6)
+# size of the per-device scratch array of mla_decode_step_noalloc
+MLA_NOALLOC_SCRATCH_BYTES = 64 << 20
 MLA_F32, MLA_BF16 = 0, 1
 
 # every symbol include/mla.h declares
 EXPORTS = ("mla_absorb_q", "mla_decode_absorbed", "mla_splitkv_combine", "mla_out_uv",
            "gqla_decode_gqa", "gqla_expand_cache", "mla_cache_append", "mla_decode_step",
-           "gqla_decode_step", "mla_project_q", "mla_fold_q_weights", "mla_project_q_folded",
+           "mla_decode_step_noalloc", "gqla_decode_step", "mla_project_q", "mla_fold_q_weights", "mla_project_q_folded",
            "mla_out_project", "mla_fold_o_weights", "mla_out_project_folded",
            "mla_cache_scalars_per_token", "gqla_cache_scalars_per_token",
            "mla_decode_kernel_kind", "gqla_decode_kernel_kind", "mla_checked_bad_pages",
@@ -70,6 +72,7 @@ def load(checked=False):
             "gqla_expand_cache": [S, P, P, P, P, P, P, P],
             "mla_cache_append": [S, ctypes.c_int32, ctypes.c_float, P, P, P, P, P, P, P],
             "mla_decode_step": [S, P, P, P, P, P, P, P, P, P, P, P, P, P],
+            "mla_decode_step_noalloc": [S, P, P, P, P, P, P, P, P, P],
             "gqla_decode_step": [S, P, P, P, P, P, P, P, P, P, P, P],
             "mla_project_q": [S, ctypes.c_int32, ctypes.c_float, P, P, P, P, P],
             "mla_fold_q_weights": [S, ctypes.c_int32, P, P, P, P],
@@ -182,6 +185,12 @@ def mla_decode_step(shape, q, w_uk, w_uv, kv_pool, page_table, ctx_lens, q_abs, 
     return _call("mla_decode_step", shape,
                  (q, w_uk, w_uv, kv_pool, page_table, ctx_lens, q_abs, o_part, lse_part,
                   o_lat, out, lse), stream, check)
+
+
+def mla_decode_step_noalloc(shape, q, w_uk, w_uv, kv_pool, page_table, ctx_lens, out,
+                            lse=None, stream=None, check=True):
+    return _call("mla_decode_step_noalloc", shape,
+                 (q, w_uk, w_uv, kv_pool, page_table, ctx_lens, out, lse), stream, check)
 
 
 def gqla_decode_step(shape, q, k_pool, v_pool, kr_pool, page_table, ctx_lens, o_part,

@@ -1,11 +1,19 @@
-// C ABI of libmla: argument validation, kernel selection and the two step helpers.
+// C ABI of libmla: argument validation, kernel selection and the step helpers.
 // Every check runs on the host before any HIP call; the library allocates nothing.
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "mla.h"
+
+// Workspaces of mla_decode_step_noalloc (q_abs, o_part, lse_part, o_lat of one step).
+// Each device that runs the library holds its own copy until the process ends.  In host
+// code this name is only a handle for hipGetSymbolAddress, never a device address.
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -70,6 +78,48 @@ mla_status_t validate(const mla_shape_t* s) {
 
 mla_status_t hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// Byte offsets of the step's workspaces inside the scratch array, each rounded up to 256.
+struct StepScratch {
+  int64_t q_abs, o_part, lse_part, o_lat, total;
+};
+
+StepScratch step_scratch_layout(const mla_shape_t& s) {
+  auto up = [](int64_t x) { return (x + 255) & ~static_cast<int64_t>(255); };
+  const int64_t rows = static_cast<int64_t>(s.batch) * s.s_q * s.n_heads;
+  const int64_t es = s.dtype == MLA_BF16 ? 2 : 4;
+  StepScratch l;
+  l.q_abs = 0;
+  l.o_part = up(rows * (s.d_c + s.d_rope) * es);
+  l.lse_part = l.o_part + up(rows * s.n_splits * s.d_c * 4);
+  l.o_lat = l.lse_part + up(rows * s.n_splits * 4);
+  l.total = l.o_lat + up(rows * s.d_c * 4);
+  return l;
+}
+
+// Device address of the scratch array on each device, looked up once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch array's device address on the current device.
+mla_status_t current_scratch(unsigned char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+        return MLA_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = static_cast<unsigned char*>(p);
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,6 +131,8 @@ const char* mla_status_str(mla_status_t st) {
     case MLA_ERR_SHAPE: return "invalid or inconsistent shape";
     case MLA_ERR_UNSUPPORTED: return "unsupported dimensions, dtype or page size";
     case MLA_ERR_HIP: return "HIP launch or runtime error";
+    case MLA_ERR_TOO_LARGE:
+      return "workspaces exceed the fixed scratch of mla_decode_step_noalloc";
   }
   return "unknown status";
 }
@@ -277,6 +329,25 @@ mla_status_t mla_decode_step(const mla_shape_t* s, const void* q, const void* w_
   v = mla_splitkv_combine(s, s->d_c, o_part, lse_part, o_lat, lse, stream);
   if (v != MLA_OK) return v;
   return mla_out_uv(s, o_lat, w_uv, out, stream);
+}
+
+mla_status_t mla_decode_step_noalloc(const mla_shape_t* s, const void* q, const void* w_uk,
+                                     const void* w_uv, const void* kv_pool,
+                                     const int32_t* page_table, const int32_t* ctx_lens,
+                                     float* out, float* lse, hipStream_t stream) {
+  mla_status_t v = validate(s);
+  if (v != MLA_OK) return v;
+  if (!q || !w_uk || !w_uv || !kv_pool || !page_table || !ctx_lens || !out)
+    return MLA_ERR_NULL;
+  const StepScratch l = step_scratch_layout(*s);
+  if (l.total > MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_TOO_LARGE;
+  unsigned char* base = nullptr;
+  v = current_scratch(&base);
+  if (v != MLA_OK) return v;
+  return mla_decode_step(s, q, w_uk, w_uv, kv_pool, page_table, ctx_lens, base + l.q_abs,
+                         reinterpret_cast<float*>(base + l.o_part),
+                         reinterpret_cast<float*>(base + l.lse_part),
+                         reinterpret_cast<float*>(base + l.o_lat), out, lse, stream);
 }
 
 mla_status_t gqla_decode_step(const mla_shape_t* s, const void* q, const void* k_pool,

@@ -16,8 +16,9 @@
  *
  * Conventions shared by every entry point
  *  - All tensor arguments are DEVICE pointers owned by the caller; the library allocates
- *    nothing and never synchronises (the checked build's bad-page flag, below, is its only
- *    global state, and mla_checked_bad_pages its only synchronous call).  Every call is asynchronous
+ *    nothing and never synchronises (its only global state is the fixed scratch array of
+ *    mla_decode_step_noalloc and the checked build's bad-page flag, below;
+ *    mla_checked_bad_pages is its only synchronous call).  Every call is asynchronous
  *    on `stream` (0 = the null stream).  Tensors are dense, row-major, in the layouts
  *    given below; `dtype` (MLA_F32 or MLA_BF16) is the element type of q, q_abs, the
  *    caches and the weights.  Split partials, latent outputs and final outputs are fp32.
@@ -55,7 +56,9 @@ typedef enum {
   MLA_ERR_NULL = 1,        /* a required pointer is NULL                                 */
   MLA_ERR_SHAPE = 2,       /* a size is non-positive or inconsistent                     */
   MLA_ERR_UNSUPPORTED = 3, /* valid but not implemented (dims, dtype, page size)         */
-  MLA_ERR_HIP = 4          /* a HIP launch or runtime call failed                        */
+  MLA_ERR_HIP = 4,         /* a HIP launch or runtime call failed                        */
+  MLA_ERR_TOO_LARGE = 5    /* the step's workspaces exceed mla_decode_step_noalloc's
+                              fixed scratch (MLA_NOALLOC_SCRATCH_BYTES)                  */
 } mla_status_t;
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
@@ -221,6 +224,28 @@ mla_status_t mla_decode_step(const mla_shape_t* shape, const void* q, const void
                              const int32_t* page_table, const int32_t* ctx_lens,
                              void* q_abs, float* o_part, float* lse_part, float* o_lat,
                              float* out, float* lse, hipStream_t stream);
+
+/* Size of the scratch array that mla_decode_step_noalloc uses on each device: 64 MiB. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+
+/* mla_decode_step without caller workspaces, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, kernels and results as mla_decode_step (out and lse
+ * bitwise equal), but q_abs, o_part, lse_part and o_lat live in one file-scope device
+ * array of MLA_NOALLOC_SCRATCH_BYTES that each device running the library holds from its
+ * first use until the process ends.  The workspaces, each rounded up to 256 bytes, must
+ * fit: rows = B*s_q*H, rows*(d_c+d_rope)*sizeof(dtype) + rows*S*d_c*4 + rows*S*4 +
+ * rows*d_c*4 <= MLA_NOALLOC_SCRATCH_BYTES, else MLA_ERR_TOO_LARGE and nothing runs
+ * (e.g. B = 4, H = 128, S = 32 at bf16 takes 33.6 MiB; B = 64, s_q = 2, H = 128, S = 6
+ * does not fit).  Allocates nothing: the array's device address is looked up once per
+ * device (hipGetSymbolAddress, on the first call with that device current).  Every call on
+ * one device shares that device's array and leaves its workspaces there: calls that
+ * overlap in time on one device (different streams or host threads without ordering)
+ * race and give meaningless results; calls ordered on one stream are safe. */
+mla_status_t mla_decode_step_noalloc(const mla_shape_t* shape, const void* q,
+                                     const void* w_uk, const void* w_uv, const void* kv_pool,
+                                     const int32_t* page_table, const int32_t* ctx_lens,
+                                     float* out, float* lse, hipStream_t stream);
 
 /* Whole GQA-path step a5 -> a3 on one stream: o_part [B,s_q,H,S,d_v] and lse_part are
  * caller workspaces; out [B,s_q,H,d_v] fp32, lse [B,s_q,H] fp32 (may be NULL). */

@@ -184,3 +184,31 @@ def test_projection_arguments_checked():
 def test_kernel_kind_is_host_only():
     assert mla.mla_decode_kernel_kind(good_shape()) in (0, 1)
     assert mla.gqla_decode_kernel_kind(good_shape(n_wheads=2)) in (0, 1)
+
+
+def test_noalloc_step_rejects_workspaces_beyond_its_scratch():
+    """mla_decode_step_noalloc checks that q_abs, o_part, lse_part and o_lat (each rounded up
+    to 256 bytes) fit its fixed scratch before it looks the scratch up or launches."""
+    fake = 0x1000
+
+    def need(B, s_q, H, S, d_c=512, d_rope=64, es=2):
+        up = lambda x: -(-x // 256) * 256   # noqa: E731
+        rows = B * s_q * H
+        return (up(rows * (d_c + d_rope) * es) + up(rows * S * d_c * 4) + up(rows * S * 4)
+                + up(rows * d_c * 4))
+
+    dims = dict(d_c=512, d_rope=64, d_nope=128, d_v=128, n_heads=128, n_wheads=128,
+                dtype="bf16", max_pages=2048, num_pages=8192)
+    args = (fake,) * 7
+    for B, s_q, S in ((8, 1, 32), (64, 2, 6)):   # 8 x 128 heads x 32 splits; ragged MTP
+        assert need(B, s_q, 128, S) > mla.MLA_NOALLOC_SCRATCH_BYTES
+        s = good_shape(batch=B, s_q=s_q, n_splits=S, **dims)
+        assert mla.mla_decode_step_noalloc(s, *args, fake, stream=0,
+                                           check=False) == mla.MLA_ERR_TOO_LARGE
+    assert need(7, 1, 128, 32) <= mla.MLA_NOALLOC_SCRATCH_BYTES   # the largest B that fits
+    s = good_shape(batch=4, n_splits=32, **dims)
+    assert mla.mla_decode_step_noalloc(s, *args[:6], None, fake, stream=0,   # out NULL
+                                       check=False) == mla.MLA_ERR_NULL
+    assert mla.mla_decode_step_noalloc(good_shape(batch=0), *args, fake, stream=0,
+                                       check=False) == mla.MLA_ERR_SHAPE
+    assert "scratch" in mla.mla_status_str(mla.MLA_ERR_TOO_LARGE)
