@@ -170,6 +170,113 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
   }
 }
 
+// a1 for a few bf16 queries (at most 8 per block), the weight read streamed at full width.
+// Block (head h, 256 latent columns c0 .., QB queries), 256 threads, one block per CU at 128
+// heads.  Lane l of wave wv owns columns c0 + 8 (l % 32) .. +8 and the weight rows
+// i = l / 32 + 2 (wv + 4 j), j = 0 .. d_n / 8 - 1: each load instruction reads two whole
+// 512-byte row segments, and a thread's d_n / 8 row loads are all issued at the start,
+// right after the queries' (which the products need first), so the products of row j start
+// as soon as its load lands instead of after the whole weight slice.  The two row halves of
+// a wave meet by a lane swap, the four waves in LDS (summed in wave order).
+constexpr int kAsC = 256;   // latent columns per block
+template <int QB>
+__global__ __launch_bounds__(256) void absorb_q_stream_kernel(const bf16_t* __restrict__ q,
+                                                              const bf16_t* __restrict__ w_uk,
+                                                              bf16_t* __restrict__ q_abs,
+                                                              int NQ, int H, int Hw, int d_r,
+                                                              int d_c) {
+  constexpr int d_n = 128, kRowsT = d_n / 8;
+  __shared__ __align__(16) float qs[d_n * QB];          // [row i][query]
+  __shared__ __align__(16) float red[4][QB][kAsC];      // per-wave partial sums
+  const int h = blockIdx.x, c0 = blockIdx.y * kAsC, q0 = blockIdx.z * QB;
+  const int w = h / (H / Hw);
+  const int nq = min(QB, NQ - q0);
+  const int dq = d_n + d_r, D = d_c + d_r;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int cc = lane & 31, rp = lane >> 5;
+  // (1) the queries' no-position parts: QB * d_n / 8 threads load 8 elements each
+  uint4 qraw = make_uint4(0u, 0u, 0u, 0u);
+  const int jq = tid / (d_n / 8), i8 = 8 * (tid % (d_n / 8));
+  const bool qload = tid < QB * d_n / 8 && jq < nq;
+  if (qload)
+    qraw = *reinterpret_cast<const uint4*>(q + (static_cast<size_t>(q0 + jq) * H + h) * dq + i8);
+  // (2) every weight row of this thread, in flight together
+  const bf16_t* W = w_uk + static_cast<size_t>(w) * d_n * d_c + c0 + 8 * cc;
+  uint4 raw[kRowsT];
+#pragma unroll
+  for (int j = 0; j < kRowsT; ++j)
+    raw[j] = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(rp + 2 * (wv + 4 * j)) * d_c);
+  // (3) the queries into LDS, transposed
+  if (tid < QB * d_n / 8) {
+    const uint32_t u[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qs[(i8 + 2 * e) * QB + jq] = __uint_as_float(u[e] << 16);
+      qs[(i8 + 2 * e + 1) * QB + jq] = __uint_as_float(u[e] & 0xffff0000u);
+    }
+  }
+  __syncthreads();
+  float acc[QB][8];
+#pragma unroll
+  for (int k = 0; k < QB; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
+  // (4) row by row in load order
+#pragma unroll
+  for (int j = 0; j < kRowsT; ++j) {
+    const int i = rp + 2 * (wv + 4 * j);
+    const uint32_t u[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+    float wf[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wf[2 * e] = __uint_as_float(u[e] << 16);
+      wf[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+    }
+    float qv[QB];
+#pragma unroll
+    for (int k4 = 0; k4 < QB; k4 += 4) {
+      const float4 t = *reinterpret_cast<const float4*>(&qs[i * QB + k4]);
+      qv[k4] = t.x; qv[k4 + 1] = t.y; qv[k4 + 2] = t.z; qv[k4 + 3] = t.w;
+    }
+#pragma unroll
+    for (int k = 0; k < QB; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[k][e] = fmaf(qv[k], wf[e], acc[k][e]);
+  }
+  // (5) the two row halves of the wave (lanes l and l + 32), then the four waves
+#pragma unroll
+  for (int k = 0; k < QB; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[k][e]),
+                                                      __float_as_uint(acc[k][e]), false, false);
+      acc[k][e] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  if (rp == 0) {
+#pragma unroll
+    for (int k = 0; k < QB; ++k) {
+      *reinterpret_cast<float4*>(&red[wv][k][8 * cc]) =
+          make_float4(acc[k][0], acc[k][1], acc[k][2], acc[k][3]);
+      *reinterpret_cast<float4*>(&red[wv][k][8 * cc + 4]) =
+          make_float4(acc[k][4], acc[k][5], acc[k][6], acc[k][7]);
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < QB * kAsC; idx += 256) {
+    const int k = idx / kAsC, c = idx - k * kAsC;
+    if (k >= nq) break;
+    const float v = ((red[0][k][c] + red[1][k][c]) + red[2][k][c]) + red[3][k][c];
+    q_abs[(static_cast<size_t>(q0 + k) * H + h) * D + c0 + c] = f32_to_bf16(v);
+  }
+  if (blockIdx.y == 0) {
+    for (int idx = tid; idx < nq * d_r; idx += 256) {
+      const int k = idx / d_r, r = idx - k * d_r;
+      const size_t qrow = static_cast<size_t>(q0 + k) * H + h;
+      q_abs[qrow * D + d_c + r] = q[qrow * dq + d_n + r];
+    }
+  }
+}
+
 // a1 on the matrix cores (bf16, d_n = 128, 16 or more queries).  Block (head h, 128 latent
 // columns c0 .., 32 NB queries q0 ..), 4 waves; wave w computes q_abs^T[c0 + 32 w + m][q] =
 // sum_i W_UK[h][i][c] q[q][i] with v_mfma_f32_32x32x16_bf16: the weight slice, staged once in
@@ -296,10 +403,13 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
       if (u0 + b < S)
         v[b] = *reinterpret_cast<const float4*>(op + static_cast<size_t>(u0 + b) * width + c);
   };
+  // this thread's first chunk lse is loaded before the partials: loads complete in issue
+  // order, so the weight reduction below waits for it alone, not for the whole batch
+  const float l_first = static_cast<int>(threadIdx.x) < S ? lp[threadIdx.x] : -INFINITY;
   if (4 * threadIdx.x < width) issue(4 * threadIdx.x, 0);
   // row maximum and sum of the chunk weights, every thread taking splits t, t + 128, ...
-  float m = -INFINITY;
-  for (int u = threadIdx.x; u < S; u += blockDim.x) m = fmaxf(m, lp[u]);
+  float m = l_first;
+  for (int u = threadIdx.x + blockDim.x; u < S; u += blockDim.x) m = fmaxf(m, lp[u]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   if (lane == 0) red[0][wv] = m;
@@ -313,7 +423,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   const float ml = m * kLog2e;
   float tot = 0.f;
   for (int u = threadIdx.x; u < S; u += blockDim.x) {
-    const float e = exp2f(fmaf(lp[u], kLog2e, -ml));
+    const float e = exp2f(fmaf(u == static_cast<int>(threadIdx.x) ? l_first : lp[u], kLog2e, -ml));
     if (u < kCombWts) wts[u] = e;
     tot += e;
   }
@@ -511,7 +621,7 @@ __global__ __launch_bounds__(64 * kUvmWaves) void out_uv_mfma_kernel(
 //   up-projection; all waves share the merge (4 queries x 512 columns per pass), which
 //   both halves compute (only half 0 stores o_lat and lse).
 constexpr int kFuQ = 32;          // queries per block
-constexpr int kFuBatch = 16;      // partial loads per thread in flight at once
+constexpr int kFuBatch = 32;      // partial loads per thread in flight at once
 constexpr int kFuRow = 512 + 8;   // bf16 elements per LDS row of merged latents (padded)
 
 __global__ __launch_bounds__(512) void combine_out_uv_kernel(
@@ -532,6 +642,15 @@ __global__ __launch_bounds__(512) void combine_out_uv_kernel(
   const int m = lane & 31, g = lane >> 5, vb = wave & 1, kq = wave >> 1;
   const int v0 = 64 * half + 32 * vb;   // this wave's first value row
 
+  // (0) the chunk lse of this wave's queries (step 3), loaded first: loads complete in
+  // issue order, so step 3 then waits for these alone, not for the weights and partials
+  float lq[kFuQ / 8];
+#pragma unroll
+  for (int i = 0; i < kFuQ / 8; ++i) {
+    const int n = wave + 8 * i;
+    lq[i] = (n < nqb && lane < S) ? lse_part[(static_cast<size_t>(q0 + n) * H + h) * S + lane]
+                                  : -INFINITY;
+  }
   // (1) this wave's weight rows: its quarter's 8 K-steps of 16 latent columns, in flight
   uint4 a[8];
   {
@@ -551,9 +670,10 @@ __global__ __launch_bounds__(512) void combine_out_uv_kernel(
   };
   if (cq < nqb) issue(cq, 0);
   // (3) chunk weights, 1 / sum and lse of every query: one wave per query, lane = split
-  for (int n = wave; n < kFuQ; n += 8) {
-    float l = -INFINITY;
-    if (n < nqb && lane < S) l = lse_part[(static_cast<size_t>(q0 + n) * H + h) * S + lane];
+#pragma unroll
+  for (int i = 0; i < kFuQ / 8; ++i) {
+    const int n = wave + 8 * i;
+    const float l = lq[i];
     float mx = l;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
@@ -737,6 +857,22 @@ hipError_t launch_absorb_q(const mla_shape_t& s, const void* q, const void* w_uk
                          static_cast<bf16_t*>(q_abs), NQ, s.n_heads, s.n_wheads, s.d_nope,
                          s.d_rope, s.d_c);
   };
+  // fewer bf16 queries with 128-wide no-position parts: the streaming kernel
+  if (s.dtype == MLA_BF16 && s.d_nope == 128 && s.d_c % kAsC == 0 && NQ < 16) {
+    auto sk = [&](auto qbc) {
+      constexpr int QB = decltype(qbc)::value;
+      dim3 grid(s.n_heads, s.d_c / kAsC, (NQ + QB - 1) / QB);
+      hipLaunchKernelGGL((absorb_q_stream_kernel<QB>), grid, dim3(256), 0, st,
+                         static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(w_uk),
+                         static_cast<bf16_t*>(q_abs), NQ, s.n_heads, s.n_wheads, s.d_rope,
+                         s.d_c);
+    };
+    if (NQ <= 4)
+      sk(std::integral_constant<int, 4>{});
+    else
+      sk(std::integral_constant<int, 8>{});
+    return hipGetLastError();
+  }
   // 16 or more bf16 queries with 128-wide no-position parts: the matrix-core kernel
   if (s.dtype == MLA_BF16 && s.d_nope == 128 && s.d_c % kAmC == 0 && NQ >= 16) {
     auto mf = [&](auto nbc) {
