@@ -11,7 +11,7 @@
 // halves of 32 tokens (Y^T[out][token] = W[out][:] . X^T[:][token], so both operands are read
 // along the latent, the layout they have in memory), each loaded one half ahead into
 // registers.  Outputs are staged through LDS and written as whole 256-byte K and V rows
-// while the next half's MFMAs run; one barrier per half page.  The G groups of a page range run on the same XCD
+// at the start of the next half, before its loads; one barrier per half page.  The G groups of a page range run on the same XCD
 // (workgroups 8 apart), so each page is fetched from HBM once and shared through its L2.
 #include <type_traits>
 
@@ -77,6 +77,12 @@ __global__ __launch_bounds__(256, 1) void expand_mfma_kernel(
     for (int ks = 0; ks < kLat / 16; ++ks)
       wreg[ob][ks] = *reinterpret_cast<const bf16x8*>(row + 16 * ks + 8 * g);
   }
+  // Wait for the weight rows here, once (s_waitcnt vmcnt(0)).  Without it the compiler's
+  // wait analysis, merging the loop's first entry (weights still in flight) with its back
+  // edge, keeps a descending series of vmcnt waits on them inside the MFMA loop, and in
+  // every later half those waits force the next half's loads to land mid-loop, so loads
+  // and MFMAs ran one after the other.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // each wave stages tokens 8 wave .. 8 wave + 7 of a half page, one 1-KB latent row per
   // load, and their RoPE keys in one more load (lane l: token l / 8, 16-byte chunk l % 8;
@@ -103,9 +109,9 @@ __global__ __launch_bounds__(256, 1) void expand_mfma_kernel(
       stg[i] = *(reinterpret_cast<const u32x4*>(pool + (tok0 + i) * D) + lane);
     stg[8] = *reinterpret_cast<const u32x4*>(pool + (tok0 + kr_tok) * D + kr_ofs);
   };
-  // the outputs of half h - 1 (staged in y[(h - 1) & 1]) leave in four steps spread over
-  // half h's MFMAs: 64 rows of 256 bytes (token t: its K row, then its V row), 16 lanes
-  // per row, one 16-byte store per lane and step
+  // the outputs of half h - 1 (staged in y[(h - 1) & 1]) leave in four steps at the start
+  // of half h: 64 rows of 256 bytes (token t: its K row, then its V row), 16 lanes per row,
+  // one 16-byte store per lane and step
   auto store_step = [&](int hprev, int it) {
     const size_t tok0 = static_cast<size_t>(p0 + (hprev >> 1)) * 64 + 32 * (hprev & 1);
     const int row = 16 * it + (threadIdx.x >> 4);
@@ -142,6 +148,13 @@ __global__ __launch_bounds__(256, 1) void expand_mfma_kernel(
       for (int it = 0; it < 4; ++it) store_step(h - 1, it);
       return true;
     }
+    // the outputs of half h - 1 leave before the loads of half h + 1 are issued: the memory
+    // counter retires in issue order, so the staging of half h + 1 (which waits for its
+    // loads) then never waits for these stores, which have the whole MFMA loop to complete
+    if (h > 0) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) store_step(h - 1, it);
+    }
     load_half(h + 1);
     f32x16 acc[2] = {};
     const char* bt = sm.x[P] + n32 * kXRowB;
@@ -159,7 +172,6 @@ __global__ __launch_bounds__(256, 1) void expand_mfma_kernel(
       acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wreg[1][ks], bbuf[ks % kBPF], acc[1],
                                                        0, 0, 0);
       if (ks + kBPF < kLat / 16) bbuf[ks % kBPF] = read_b(ks + kBPF);
-      if (h > 0 && (ks & 7) == 4) store_step(h - 1, ks >> 3);
       __builtin_amdgcn_sched_barrier(0);
     }
     // lane (n32, g) holds token n32, outputs 32 ob + 8 q + 4 g + 0..3 of the wave's 64
