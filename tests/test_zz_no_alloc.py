@@ -84,3 +84,41 @@ def test_noalloc_step_matches_step_on_two_calls(case):
         if i == 1:
             check_against_oracle(inp, out, lse)
         del d
+
+
+def test_noalloc_step_replays_under_graph_capture():
+    """The allocation-free step is capturable in a HIP graph (no allocation, no memset in
+    it): five replays, each followed by an eager step, all bitwise equal to the eager
+    result, and the eager step matches the oracle."""
+    cfg = get_config("dsv2-b16-t4096", batch=3, ctx=("list", [2100, 700, 5]))
+    inp = make_inputs(cfg, seed=5)
+    d = DeviceInputs(inp)
+    announce(f"noalloc graph capture: {cfg.name} B={cfg.batch} ctx={list(inp.ctx_lens)}")
+
+    def step():
+        mla.mla_decode_step_noalloc(d.shape, d.q, d.w_uk, d.w_uv, d.pool, d.page_table,
+                                    d.ctx_lens, d.out, d.lse)
+
+    step()
+    torch.cuda.synchronize()
+    want = (d.out.clone(), d.lse.clone())
+    check_against_oracle(inp, want[0], want[1])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(5):
+        d.out.fill_(float("nan"))
+        d.lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.out, want[0]) and torch.equal(d.lse, want[1]), f"replay {r}"
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(d.out, want[0]), f"eager step after replay {r}"
