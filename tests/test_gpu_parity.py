@@ -491,7 +491,7 @@ def test_full_gqla_b32_t65536_gqa_path(name):
     assert lse_abs <= LSE_ABS["bf16"]
 
 
-# ------------------------------------------- reference moves (online-softmax rerun path)
+# ------------------------------------ reference moves (online-softmax rescale path)
 
 @pytest.mark.parametrize("slack", ["0", "0.25"])
 def test_reference_moves_rescale_path(slack, monkeypatch):
