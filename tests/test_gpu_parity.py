@@ -174,6 +174,29 @@ def test_bf16_step_entry_point_matches_steps(name, s_q, ctx, S):
 
 
 
+@pytest.mark.parametrize("H,Hw,s_q", [(96, 96, 1), (160, 160, 1), (64, 64, 3), (32, 8, 3)])
+def test_odd_row_block_counts(H, Hw, s_q):
+    """Query rows per sequence (s_q x H) that give the matrix-core kernels an odd number of
+    row blocks, so the workgroup-to-(chunk, row block) mapping and the output row offsets
+    are exercised beyond the two blocks of the 128-head shapes: 96 and 160 rows (32-row
+    blocks, 3 and 5), 192 rows (64-row blocks, 3) and GQLA-style grouped heads at s_q = 3
+    (96 rows, 4 query heads per weight head).  Every step against the oracle, then the step
+    entry point against the separate entry points bit for bit."""
+    cfg = small(n_heads=H, n_wheads=Hw, s_q=s_q, batch=3, ctx=("list", [700, 130, 197]))
+    inp = make_inputs(cfg, seed=31)
+    check_absorbed_all_steps(inp, S=4)
+    d = DeviceInputs(inp, n_splits=4)
+    absorbed_step(d)
+    want = [t.clone() for t in (d.out, d.lse, d.o_lat)]
+    for t in (d.out, d.lse, d.o_lat):
+        t.fill_(7.0)
+    mla.mla_decode_step(d.shape, d.q, d.w_uk, d.w_uv, d.pool, d.page_table, d.ctx_lens,
+                        d.q_abs, d.o_part, d.lse_part, d.o_lat, d.out, d.lse)
+    torch.cuda.synchronize()
+    for got, exp, what in zip((d.out, d.lse, d.o_lat), want, ("out", "lse", "o_lat")):
+        assert torch.equal(got, exp), f"{what} differs from the separate entry points"
+
+
 @pytest.mark.parametrize("name,batch,s_q", [
     ("dsv2-b16-t4096", 3, 1), ("dsv2-b16-t4096", 12, 1), ("dsv2-b16-t4096", 17, 1),
     ("dsv2-b16-t4096", 33, 1), ("dsv2-b16-t4096", 50, 2), ("dsv2-b16-t4096", 65, 2),
