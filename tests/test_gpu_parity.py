@@ -406,6 +406,39 @@ def test_gqla_expand_and_gqa_path(dtype, ctx, S):
     assert lse_abs <= LSE_ABS[cfg.dtype]
 
 
+@pytest.mark.parametrize("H,G,s_q,kind", [(16, 16, 1, 1), (32, 16, 1, 1), (64, 4, 1, 1),
+                                           (24, 3, 2, 1), (40, 5, 1, 1), (64, 2, 1, 0)])
+def test_gqa_path_group_counts(H, G, s_q, kind):
+    """The GQA path (a6 then a5 + a3) at other group shapes: one, two and sixteen query
+    rows per group (16 is the matrix-core kernel's limit), odd group counts (3 and 5, which
+    also give the expansion kernel page ranges that are not a power of two), and 32 rows per
+    group, which takes the generic kernel; against the oracle's expansion and the plain
+    definition."""
+    cfg = get_config("gqla-b32-t8192", n_heads=H, n_wheads=G, s_q=s_q, batch=3,
+                     ctx=("list", [700, 130, 65]), n_splits=3)
+    inp = make_inputs(cfg, seed=41)
+    announce(f"case gqa groups H={H} G={G} s_q={s_q}")
+    d = DeviceInputs(inp)
+    assert mla.gqla_decode_kernel_kind(d.shape) == kind
+    k, v, kr = expanded_pools(d)
+    mla.gqla_expand_cache(d.shape, d.pool, d.w_uk, d.w_uv, k, v, kr)
+    torch.cuda.synchronize()
+    ek, ev, ekr = ref.expand_cache(inp.pool_f32(), inp.w_uk, inp.w_uv, cfg.d_c)
+    fin = np.isfinite(ek)
+    gk = k.float().cpu().numpy()
+    assert np.array_equal(np.isfinite(gk), fin)
+    assert rel_err(gk[fin], ek[fin]) <= TOL["bf16"]
+    gv = v.float().cpu().numpy()
+    assert rel_err(gv[np.isfinite(ev)], ev[np.isfinite(ev)]) <= TOL["bf16"]
+    gqa_step(d, k, v, kr)
+    out, lse = ref.mla_decode_naive(inp.q, inp.pool_view(), inp.page_table, inp.ctx_lens,
+                                    inp.w_uk, inp.w_uv, cfg.scale, cfg.page_size, cfg.d_c)
+    e_out, e_lse = rel_err(d.out.cpu().numpy(), out), rel_err(d.lse.cpu().numpy(), lse)
+    announce(f"  gqa errors out={e_out:.3e} lse={e_lse:.3e}")
+    assert e_out <= TOL["bf16"] and e_lse <= TOL["bf16"]
+    assert lse_abs_err(d.lse.cpu().numpy(), lse) <= LSE_ABS["bf16"]
+
+
 def test_gqa_path_uses_matrix_cores_at_gqla_shapes():
     for sq in (1, 2):
         cfg = get_config("gqla-b32-t8192", s_q=sq)
