@@ -63,6 +63,11 @@ CASES = {
                              ("dsv2-b16-t4096", dict(batch=3, ctx=("list", [1000, 65, 2])))),
     "f32": (("tiny-f32", dict(batch=4, ctx=("list", [500, 333, 64, 7]))),
             ("tiny-f32", dict(batch=2, ctx=("list", [40, 1])))),
+    # the largest 128-head, 32-split step the scratch holds (7 sequences: 61.7 of 64 MiB),
+    # so the workspaces reach the end of the array
+    "bf16-max-scratch": (("dsv2-b16-t4096", dict(batch=7, n_splits=32,
+                                                 ctx=("list", [4096, 2048, 700, 64, 1, 4000, 130]))),
+                         ("dsv2-b16-t4096", dict(batch=2, ctx=("list", [300, 129])))),
     "gqla-mtp": (("gqla-mtp-b32-t65536", dict(batch=6, ctx=("list", [9000, 4097, 3000, 64,
                                                                       700, 2]))),
                  ("gqla-mtp-b32-t65536", dict(batch=2, ctx=("list", [513, 2])))),
