@@ -216,9 +216,10 @@ mla_status_t mla_out_project_folded(const mla_shape_t* shape, int32_t d_model,
 /* Whole absorbed step a1 -> a2 -> a3 -> a4 on one stream.  The caller provides the
  * workspaces: q_abs [B,s_q,H,D] dtype, o_part [B,s_q,H,S,d_c] fp32,
  * lse_part [B,s_q,H,S] fp32, o_lat [B,s_q,H,d_c] fp32.  out [B,s_q,H,d_v] fp32,
- * lse [B,s_q,H] fp32 (may be NULL).  For bf16 with d_c = 512, d_v = 128, S <= 64 and H a
- * multiple of 8, a3 and a4 run as one kernel; out, lse and o_lat are then bitwise those
- * of the separate entry points. */
+ * lse [B,s_q,H] fp32 (may be NULL).  For bf16 with d_c = 512, d_v = 128, S <= 64, H a
+ * multiple of 8 and 2 H ceil(B s_q / 32) >= 256 (enough workgroups to fill the GPU), a3 and
+ * a4 run as one kernel; out, lse and o_lat are bitwise those of the separate entry points
+ * either way. */
 mla_status_t mla_decode_step(const mla_shape_t* shape, const void* q, const void* w_uk,
                              const void* w_uv, const void* kv_pool,
                              const int32_t* page_table, const int32_t* ctx_lens,

@@ -151,8 +151,9 @@ def test_bf16_step_entry_point_matches_steps(name, s_q, ctx, S):
     """At bf16 with d_c 512 and d_v 128 the step entry point merges the splits and
     up-projects in one kernel; its outputs must equal those of the separate entry points
     bit for bit (20 sequences at s_q = 2 give two query blocks of 32, the second ragged;
-    s_q = 2 over one token gives rows with no visible token; 4 heads take the separate
-    kernels inside the step), and match the oracle."""
+    s_q = 2 over one token gives rows with no visible token; the 32- and 4-head shapes have
+    too few workgroups for the fused kernel and take the separate kernels inside the step),
+    and match the oracle."""
     cfg = get_config(name, batch=len(ctx), s_q=s_q, ctx=("list", ctx))
     inp = make_inputs(cfg, seed=21)
     announce(f"case {name} s_q={s_q} ctx={ctx[:6]} S={S}")
