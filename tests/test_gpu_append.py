@@ -147,3 +147,38 @@ def test_decode_over_the_appended_cache():
     announce(f"  decode after append rel_err {e:.3e}")
     assert e <= TOL["bf16"]
     assert np.array_equal(np.isneginf(d.lse.cpu().numpy()), np.isneginf(lse))
+
+
+def test_decode_loop_across_page_boundaries():
+    """Four decode steps in a row, each appending one new token per sequence and then
+    decoding over the grown cache, with new tokens that cross page boundaries (positions
+    63 -> 66 and 127 -> 130) and one long sequence; every step against the oracle's decode over the
+    oracle's cache after the same appends (rows rounded to bf16 as the GPU stores them)."""
+    from workloads.gen import bf16_round
+    final = [67, 131, 504]
+    cfg = get_config("dsv2-b16-t4096", batch=3, s_q=1, ctx=("list", final), n_splits=3)
+    inp = make_inputs(cfg, seed=37)
+    ap = make_append_inputs(cfg, seed=37)
+    d = DeviceInputs(inp)
+    w_dkv, w_kr = to_dev(ap.w_dkv, cfg.dtype), to_dev(ap.w_kr, cfg.dtype)
+    pool_ref = inp.pool_f32().astype(np.float64)
+    rng = np.random.default_rng(np.random.SeedSequence([37, 9]))
+    for k in range(4):
+        T = np.array([f - 3 + k for f in final], dtype=np.int32)
+        announce(f"case decode loop step {k}: ctx={list(T)}")
+        d.ctx_lens.copy_(torch.from_numpy(T))
+        h = bf16_round(rng.standard_normal((cfg.batch, cfg.s_q, ap.d_model)).astype(np.float32))
+        mla.mla_cache_append(d.shape, ap.d_model, BASE, to_dev(h, cfg.dtype), w_dkv, w_kr,
+                             d.page_table, d.ctx_lens, d.pool)
+        mla.mla_decode_step(d.shape, d.q, d.w_uk, d.w_uv, d.pool, d.page_table, d.ctx_lens,
+                            d.q_abs, d.o_part, d.lse_part, d.o_lat, d.out, d.lse)
+        torch.cuda.synchronize()
+        pool_ref = ref_append.cache_append(pool_ref, inp.page_table, T, h, ap.w_dkv, ap.w_kr,
+                                           cfg.s_q, cfg.page_size, BASE)
+        pool_ref = bf16_round(pool_ref.astype(np.float32)).astype(np.float64)
+        out, lse = ref.mla_decode_naive(inp.q, pool_ref, inp.page_table, T, inp.w_uk,
+                                        inp.w_uv, cfg.scale, cfg.page_size, cfg.d_c)
+        e = float(np.max(np.abs(d.out.cpu().numpy() - out)) / np.max(np.abs(out)))
+        le = float(np.max(np.abs(d.lse.cpu().numpy() - lse)))
+        announce(f"  step {k}: out rel_err {e:.3e}, lse max abs {le:.3e}")
+        assert e <= TOL["bf16"] and le <= 1e-2
