@@ -11,6 +11,8 @@
 // fp32 (and shapes the matrix-core kernel does not take) on the vector units.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -197,6 +199,112 @@ __global__ __launch_bounds__(64 * kApmWaves) void cache_append_mfma_kernel(
   }
 }
 
+// bf16 with at most 8 new tokens: the weight read spread over D / 2 workgroups (two output
+// rows each, one RoPE pair for the key rows) instead of D / 16, since with so few tokens the
+// step is the latency of one weight read.  Thread t owns the 8-element chunks t, t + 256,
+// t + 512 of the d_model axis; every load of the thread (both weight rows and the QB hidden
+// states, the latter from L2) is issued before the first product; the partial sums meet by
+// wave sums and LDS.
+template <int QB>
+__global__ __launch_bounds__(256, 1) void cache_append_stream_kernel(
+    const bf16_t* __restrict__ h, const bf16_t* __restrict__ w_dkv,
+    const bf16_t* __restrict__ w_kr, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ ctx_lens, bf16_t* __restrict__ pool, int NQ, int s_q,
+    int d_c, int d_r, int d_model, int max_pages, int num_pages, int P, double log_base) {
+  constexpr int kCh = 3;   // chunks per thread: d_model <= 8 * 256 * 3
+  __shared__ float red[4][2 * QB];
+  const int D = d_c + d_r;
+  const int o0 = 2 * blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bf16_t* wr[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int o = o0 + r;
+    wr[r] = o < d_c ? w_dkv + static_cast<size_t>(o) * d_model
+                    : w_kr + static_cast<size_t>(o - d_c) * d_model;
+  }
+  const int n_ch = d_model / 8;
+  uint4 wv[2][kCh], hv[QB][kCh];
+#pragma unroll
+  for (int j = 0; j < kCh; ++j) {
+    const int c = min(tid + 256 * j, n_ch - 1);   // past the end: a valid chunk, not used
+#pragma unroll
+    for (int r = 0; r < 2; ++r) wv[r][j] = *reinterpret_cast<const uint4*>(wr[r] + 8 * c);
+#pragma unroll
+    for (int n = 0; n < QB; ++n)
+      hv[n][j] = *reinterpret_cast<const uint4*>(
+          h + static_cast<size_t>(min(n, NQ - 1)) * d_model + 8 * c);
+  }
+  // keep the scheduler from moving the conversions of early loads ahead of the later loads
+  __builtin_amdgcn_sched_barrier(0);
+  float acc[2][QB];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int n = 0; n < QB; ++n) acc[r][n] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kCh; ++j) {
+    // a chunk past the end contributes zero (a select, not a branch, so that the compiler
+    // keeps every load ahead of the first product)
+    const bool live = tid + 256 * j < n_ch;
+    float w[2][8];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const uint32_t u[4] = {wv[r][j].x, wv[r][j].y, wv[r][j].z, wv[r][j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[r][2 * e] = __uint_as_float(u[e] << 16);
+        w[r][2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < QB; ++n) {
+      const uint32_t u[4] = {hv[n][j].x, hv[n][j].y, hv[n][j].z, hv[n][j].w};
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = live ? __uint_as_float(u[e] << 16) : 0.f;
+        x[2 * e + 1] = live ? __uint_as_float(u[e] & 0xffff0000u) : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][n] = fmaf(w[r][e], x[e], acc[r][n]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int n = 0; n < QB; ++n) {
+      const float v = wave_sum(acc[r][n]);
+      if (lane == 0) red[wave][r * QB + n] = v;
+    }
+  __syncthreads();
+  if (tid >= QB) return;
+  // thread n: token n, both rows (a RoPE pair when o0 >= d_c)
+  const int n = tid;
+  if (n >= NQ) return;
+  float x0 = ((red[0][n] + red[1][n]) + red[2][n]) + red[3][n];
+  float x1 = ((red[0][QB + n] + red[1][QB + n]) + red[2][QB + n]) + red[3][QB + n];
+  const int b = n / s_q, s = n - b * s_q;
+  const int t = ctx_lens[b] - s_q + s;
+  if (t < 0 || t / P >= max_pages) return;
+  const int page = page_table[static_cast<size_t>(b) * max_pages + t / P];
+  if (page < 0 || page >= num_pages) return;
+  if (o0 >= d_c) {
+    const int i = (o0 - d_c) >> 1;
+    const double ang = static_cast<double>(t) * exp(-log_base * (2.0 * i) / d_r);
+    const double c = cos(ang), sn = sin(ang);
+    const float y0 = static_cast<float>(x0 * c - x1 * sn);
+    const float y1 = static_cast<float>(x0 * sn + x1 * c);
+    x0 = y0;
+    x1 = y1;
+  }
+  bf16_t* dst = pool + (static_cast<size_t>(page) * P + t % P) * D + o0;
+  dst[0] = f32_to_bf16(x0);
+  dst[1] = f32_to_bf16(x1);
+}
+
 }  // namespace
 
 hipError_t launch_cache_append(const mla_shape_t& s, int d_model, float rope_base,
@@ -206,6 +314,24 @@ hipError_t launch_cache_append(const mla_shape_t& s, int d_model, float rope_bas
   const int NQ = s.batch * s.s_q, D = s.d_c + s.d_rope;
   const dim3 grid((D + kApRows - 1) / kApRows, (NQ + kApTok - 1) / kApTok);
   const double lb = log(static_cast<double>(rope_base));
+  // few tokens: two rows per workgroup on the vector units (d_model within three chunks of
+  // 8 elements per thread)
+  if (s.dtype == MLA_BF16 && NQ <= 8 && d_model % 8 == 0 && d_model <= 8 * 256 * 3 &&
+      s.d_c % 2 == 0 && D % 2 == 0) {
+    auto go = [&](auto qbc) {
+      constexpr int QB = decltype(qbc)::value;
+      hipLaunchKernelGGL((cache_append_stream_kernel<QB>), dim3(D / 2), dim3(256), 0, st,
+                         static_cast<const bf16_t*>(h), static_cast<const bf16_t*>(w_dkv),
+                         static_cast<const bf16_t*>(w_kr), page_table, ctx_lens,
+                         static_cast<bf16_t*>(pool), NQ, s.s_q, s.d_c, s.d_rope, d_model,
+                         s.max_pages, s.num_pages, s.page_size, lb);
+    };
+    if (NQ <= 4)
+      go(std::integral_constant<int, 4>{});
+    else
+      go(std::integral_constant<int, 8>{});
+    return hipGetLastError();
+  }
   if (s.dtype == MLA_BF16 && D % 16 == 0 && d_model % 32 == 0) {
     hipLaunchKernelGGL(cache_append_mfma_kernel, dim3(D / 16, (NQ + 15) / 16),
                        dim3(64 * kApmWaves), 0, st, static_cast<const bf16_t*>(h),
