@@ -9,9 +9,13 @@
 // weight rows (W_UK[j] then W_UV[j], 512 wide) stay in registers for the whole range as the
 // A operand of v_mfma_f32_32x32x16_bf16 (64 rows per wave); pages stream through LDS in
 // halves of 32 tokens (Y^T[out][token] = W[out][:] . X^T[:][token], so both operands are read
-// along the latent, the layout they have in memory), each loaded one half ahead into
-// registers.  Outputs are staged through LDS and written as whole 256-byte K and V rows
-// at the start of the next half, before its loads; one barrier per half page.  The G groups of a page range run on the same XCD
+// along the latent, the layout they have in memory).  The latent rows go from global memory
+// straight into LDS (global_load_lds_dwordx4: no staging registers), two halves ahead,
+// through a ring of three half buffers; each wave waits for its own loads of the next half
+// with an explicit vmcnt before the half's barrier, which is a bare s_barrier: the
+// workgroup fence of __syncthreads would also wait for the loads issued after them.
+// Outputs are staged through LDS and written as whole 256-byte K and V rows at the start
+// of the next half, before its loads.  The G groups of a page range run on the same XCD
 // (workgroups 8 apart), so each page is fetched from HBM once and shared through its L2.
 #include <type_traits>
 
@@ -31,20 +35,47 @@ constexpr int kHalf = 32;          // tokens per half page
 constexpr int kXRowB = kLat * 2;   // latent bytes of one token in the staged tile
 constexpr int kYStride = 264;      // bf16 per staged output row (256 + 8: 16-byte aligned rows)
 
-constexpr int kBPF = 6;           // operand reads in flight ahead of their MFMAs
+constexpr int kKrRowB = 128;       // RoPE-key bytes of one staged token (d_rope <= 64)
+constexpr int kXBuf = 3;           // half buffers in the latent ring
+constexpr int kBPF = 6;            // operand reads in flight ahead of their MFMAs
 
 struct ExpSmem {
-  char x[2][kHalf * kXRowB];       // two half pages of latent rows (64 KB)
+  char x[kXBuf][kHalf * kXRowB];   // latent rows of three half pages (96 KB)
+  char kr[kXBuf][kHalf * kKrRowB]; // their RoPE keys (12 KB)
   bf16_t y[2][kHalf * kYStride];   // two half pages of outputs [token][k 0..127 | v 0..127]
 };
+
+// One wave-wide load straight into LDS: lane l's 16 bytes at src land at LDS byte address
+// lds + 16 l (lds is wave-uniform, in m0).  Written as inline asm so that the compiler does
+// not track these LDS writes: it cannot tell the ring slots apart and would wait for every
+// load in flight before any LDS access.  The kernel waits for them itself (explicit vmcnt
+// before the barrier that publishes a half).  The instruction has no register results.
+__device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) void*)(p)));
+}
+
+// s_waitcnt: vector-memory count n (0..63), lgkmcnt(0), expcnt left alone
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
+}
 
 // The 16-byte chunk ch of staged token t sits at chunk ch ^ (t & 15) of its row: the
 // operand reads take one chunk from each of 16 consecutive tokens (conflict-free), the
 // staging stores write whole rows.
 __device__ __forceinline__ int xswz(int t, int ch) { return ch ^ (t & 15); }
 
+// two floats to a pair of bf16, rounded to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __global__ __launch_bounds__(256, 1) void expand_mfma_kernel(
@@ -63,7 +94,7 @@ __global__ __launch_bounds__(256, 1) void expand_mfma_kernel(
   const int p1 = min(p0 + pages_per_range, num_pages);
   if (p0 >= p1) return;
   const int D = kLat + d_r;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n32 = lane & 31, g = lane >> 5;
 
   // weight rows 64 wave + 32 ob + n32 of the group's 256 (W_UK rows, then W_UV rows)
@@ -84,80 +115,106 @@ __global__ __launch_bounds__(256, 1) void expand_mfma_kernel(
   // and MFMAs ran one after the other.
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  // each wave stages tokens 8 wave .. 8 wave + 7 of a half page, one 1-KB latent row per
-  // load, and their RoPE keys in one more load (lane l: token l / 8, 16-byte chunk l % 8;
-  // lanes past the key's width re-read its last chunk, and with no key the row's first).
-  // One register buffer: the loads of half h + 1 are in flight while half h runs (a second
-  // buffer would leave no registers for the operand prefetch).  The key load is
-  // unconditional, so the compiler counts the loads in flight exactly; group 0 alone stores
-  // the keys.
-  u32x4 stg[9];
+  // each wave loads tokens 8 wave .. 8 wave + 7 of a half page, one 1-KB latent row per
+  // instruction (lane l brings 16-byte chunk l ^ (t & 15) of token t, so that LDS chunk l
+  // holds it where the swizzle puts it), and their RoPE keys in one more (lane l: token
+  // l / 8, 16-byte chunk l % 8; lanes past the key's width re-read its last chunk, and with
+  // no key the row's first).  All groups load the keys, so the count of loads in flight is
+  // the same in every workgroup; group 0 alone stores them.
   const int n_half = 2 * (p1 - p0);
   const int per = d_r / 8;
   const int kr_tok = lane >> 3;
   const int kr_ch = min(lane & 7, max(per - 1, 0));
   const int kr_ofs = per > 0 ? kLat + 8 * kr_ch : 0;
   const bool kr_lane = j == 0 && (lane & 7) < per;
-  auto load_half = [&](int h) {
-    if (h >= n_half) return;
-    const size_t tok0 = static_cast<size_t>(p0 + (h >> 1)) * 64 + 32 * (h & 1) + 8 * wave;
-    // ordinary (cached) loads: the G workgroups of this range read the same rows, and the
-    // second to seventh reads must find them in L2 (non-temporal loads measured 5.6 ms at
-    // the GQLA shape, every group refetching from HBM)
+  auto half_tok0 = [&](int h) {
+    return static_cast<size_t>(p0 + (h >> 1)) * 64 + 32 * (h & 1) + 8 * wave;
+  };
+  // load i (0..8) of half h into ring slot h % 3: i < 8 the latent row of token
+  // 8 wave + i, i = 8 the RoPE keys of the wave's 8 tokens.  Ordinary (cached) loads: the G
+  // workgroups of this range read the same rows, and all but the first must find them in L2.
+  auto load_one = [&](int h, int i) {
+    const int b = h % kXBuf;
+    const char* rows = reinterpret_cast<const char*>(pool + half_tok0(h) * D);
+    if (i < 8) {
+      const int t = 8 * wave + i;
+      load_lds16(rows + i * 2 * D + 16 * (lane ^ (t & 15)), lds_addr(&sm.x[b][0]) + t * kXRowB);
+    } else {
+      load_lds16(rows + 2 * (kr_tok * D + kr_ofs),
+                 lds_addr(&sm.kr[b][0]) + 8 * wave * kKrRowB);
+    }
+  };
+  // the outputs of half hprev (staged in ys = y[hprev & 1]) leave in four steps: 64 rows of
+  // 256 bytes (token t: its K row, then its V row), 16 lanes per row, one 16-byte store per
+  // lane and step; step it is 8 tokens further on (ostep elements)
+  const int o_t0 = threadIdx.x >> 5, o_kv = (threadIdx.x >> 4) & 1;
+  const int o_col = 8 * (threadIdx.x & 15);
+  const size_t ostep = static_cast<size_t>(8) * G * kOut;
+  auto read_outputs = [&](const bf16_t* ys, u32x4 (&val)[4]) {
+    const bf16_t* src = ys + o_t0 * kYStride + kOut * o_kv + o_col;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      stg[i] = *(reinterpret_cast<const u32x4*>(pool + (tok0 + i) * D) + lane);
-    stg[8] = *reinterpret_cast<const u32x4*>(pool + (tok0 + kr_tok) * D + kr_ofs);
+    for (int it = 0; it < 4; ++it)
+      val[it] = *reinterpret_cast<const u32x4*>(src + 8 * it * kYStride);
   };
-  // the outputs of half h - 1 (staged in y[(h - 1) & 1]) leave in four steps at the start
-  // of half h: 64 rows of 256 bytes (token t: its K row, then its V row), 16 lanes per row,
-  // one 16-byte store per lane and step
-  auto store_step = [&](int hprev, int it) {
-    const size_t tok0 = static_cast<size_t>(p0 + (hprev >> 1)) * 64 + 32 * (hprev & 1);
-    const int row = 16 * it + (threadIdx.x >> 4);
-    const int t = row >> 1, kv = row & 1, col = 8 * (threadIdx.x & 15);
-    const u32x4 val = *reinterpret_cast<const u32x4*>(sm.y[hprev & 1] + t * kYStride +
-                                                      kOut * kv + col);
-    bf16_t* dst = (kv ? vout : kout) + ((tok0 + t) * G + j) * kOut + col;
-    __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(dst));
+  auto output_dst = [&](int hprev) {
+    const size_t tok = static_cast<size_t>(p0 + (hprev >> 1)) * 64 + 32 * (hprev & 1) + o_t0;
+    return (o_kv ? vout : kout) + (tok * G + j) * kOut + o_col;
   };
-  load_half(0);
-  // one half page; P = h & 1 as a constant, so both register buffers keep fixed registers.
-  // Returns true after the last half's outputs have left (h == n_half).
-  auto half = [&](auto par, int h) -> bool {
+  // the end of half h: this wave's loads of half h + 1 have landed (the instructions issued
+  // after them, in order: the 4 output stores of half h - 1 when h > 0, group 0's key store,
+  // the 9 loads of half h + 2 when there is one; the key store is left out of the count,
+  // which only makes the wait cover it too), its output staging too; then the barrier
+  auto end_half = [&](int h) {
+    if (h + 1 >= n_half)
+      wait_vm_lgkm0<63>();
+    else if (h + 2 < n_half)
+      h > 0 ? wait_vm_lgkm0<13>() : wait_vm_lgkm0<9>();
+    else
+      h > 0 ? wait_vm_lgkm0<4>() : wait_vm_lgkm0<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // every workgroup here has n_half >= 2: its two first halves go out now
+#pragma unroll
+  for (int i = 0; i < 9; ++i) load_one(0, i);
+#pragma unroll
+  for (int i = 0; i < 9; ++i) load_one(1, i);
+  wait_vm_lgkm0<9>();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  // one half page; P = h & 1 as a constant, so the staging buffer's address is fixed
+  auto half = [&](auto par, int h) {
     constexpr int P = decltype(par)::value;
-    if (h < n_half) {
-      char* xb = sm.x[P];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = 8 * wave + i;
-        *reinterpret_cast<u32x4*>(xb + t * kXRowB + 16 * xswz(t, lane)) = stg[i];
-      }
-      if (kr_lane) {   // the shared RoPE key, copied once per token (group 0)
-        const size_t tok = static_cast<size_t>(p0 + (h >> 1)) * 64 + 32 * P + 8 * wave + kr_tok;
-        __builtin_nontemporal_store(stg[8],
-                                    reinterpret_cast<u32x4*>(krout + tok * d_r + 8 * kr_ch));
-      }
-    }
-    // half h is staged; the outputs of half h - 1 are staged, and nobody still reads the
-    // buffers that this half overwrites (x of half h - 2 was read before the previous
-    // barrier, and y of half h - 2 was written out there too)
-    __syncthreads();
-    if (h == n_half) {   // the last half's outputs
-#pragma unroll
-      for (int it = 0; it < 4; ++it) store_step(h - 1, it);
-      return true;
-    }
-    // the outputs of half h - 1 leave before the loads of half h + 1 are issued: the memory
-    // counter retires in issue order, so the staging of half h + 1 (which waits for its
-    // loads) then never waits for these stores, which have the whole MFMA loop to complete
+    const int b = h % kXBuf;
+    // half h has landed in ring slot b; the outputs of half h - 1 are staged in y[1 - P];
+    // the ring slot and staging buffer refilled below were last read before this barrier.
+    // The half's vector-memory instructions go out here, before the MFMA loop (the 4 output
+    // stores of half h - 1, group 0's key store, the 9 loads of half h + 2, in that order).
+    // Spread over the loop instead (one every other K-step), they lengthened the loop by
+    // what they saved here: the CU's vector-memory path is what they wait for.
     if (h > 0) {
+      u32x4 oval[4];
+      read_outputs(sm.y[1 - P], oval);
+      bf16_t* odst = output_dst(h - 1);
 #pragma unroll
-      for (int it = 0; it < 4; ++it) store_step(h - 1, it);
+      for (int it = 0; it < 4; ++it)
+        __builtin_nontemporal_store(oval[it], reinterpret_cast<u32x4*>(odst + it * ostep));
     }
-    load_half(h + 1);
+    if (kr_lane) {   // the shared RoPE key, copied once per token (group 0)
+      const u32x4 key = *reinterpret_cast<const u32x4*>(&sm.kr[b][0] + 8 * wave * kKrRowB +
+                                                        16 * lane);
+      __builtin_nontemporal_store(
+          key, reinterpret_cast<u32x4*>(krout + (half_tok0(h) + kr_tok) * d_r + 8 * kr_ch));
+    }
+    if (h + 2 < n_half) {
+#pragma unroll
+      for (int i = 0; i < 9; ++i) load_one(h + 2, i);
+    }
     f32x16 acc[2] = {};
-    const char* bt = sm.x[P] + n32 * kXRowB;
+    const char* bt = &sm.x[b][0] + n32 * kXRowB;
     auto read_b = [&](int ks) {
       return *reinterpret_cast<const bf16x8*>(bt + 16 * xswz(n32, 2 * ks + g));
     };
@@ -183,11 +240,21 @@ __global__ __launch_bounds__(256, 1) void expand_mfma_kernel(
         *reinterpret_cast<uint2*>(yrow + 32 * ob + 8 * q) =
             make_uint2(pack_bf16x2(acc[ob][4 * q], acc[ob][4 * q + 1]),
                        pack_bf16x2(acc[ob][4 * q + 2], acc[ob][4 * q + 3]));
-    return false;
+    end_half(h);
   };
-  for (int h = 0;; h += 2) {
-    if (half(std::integral_constant<int, 0>(), h)) break;
-    if (half(std::integral_constant<int, 1>(), h + 1)) break;
+  for (int h = 0;; h += 2) {   // n_half is even
+    half(std::integral_constant<int, 0>(), h);
+    half(std::integral_constant<int, 1>(), h + 1);
+    if (h + 2 >= n_half) break;
+  }
+  // the last half's outputs
+  {
+    u32x4 oval[4];
+    read_outputs(sm.y[(n_half - 1) & 1], oval);
+    bf16_t* odst = output_dst(n_half - 1);
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+      __builtin_nontemporal_store(oval[it], reinterpret_cast<u32x4*>(odst + it * ostep));
   }
 }
 
