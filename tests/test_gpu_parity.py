@@ -440,6 +440,32 @@ def test_gqa_path_group_counts(H, G, s_q, kind):
     assert lse_abs_err(d.lse.cpu().numpy(), lse) <= LSE_ABS["bf16"]
 
 
+@pytest.mark.parametrize("d_rope", [0, 32, 64])
+def test_gqla_expand_rope_widths(d_rope):
+    """The matrix-core expansion with a RoPE key narrower than 64 (its lanes past the key's
+    width re-read the last chunk and store nothing) and with none at all; 67 pages, so page
+    ranges of three pages (six half pages: the three-slot ring wraps), a shorter last range
+    and empty ranges past the end.  K and V against the oracle's expansion, the keys copied
+    exactly."""
+    cfg = get_config("gqla-b32-t8192", d_rope=d_rope, batch=3,
+                     ctx=("list", [3000, 1100, 65]), n_splits=3)
+    inp = make_inputs(cfg, seed=43)
+    announce(f"case expand d_rope={d_rope} pages={inp.num_pages}")
+    d = DeviceInputs(inp)
+    k, v, kr = expanded_pools(d)
+    mla.gqla_expand_cache(d.shape, d.pool, d.w_uk, d.w_uv, k, v, kr)
+    torch.cuda.synchronize()
+    ek, ev, ekr = ref.expand_cache(inp.pool_f32(), inp.w_uk, inp.w_uv, cfg.d_c)
+    fin = np.isfinite(ek)
+    gk = k.float().cpu().numpy()
+    assert np.array_equal(np.isfinite(gk), fin)
+    assert rel_err(gk[fin], ek[fin]) <= TOL["bf16"]
+    gv = v.float().cpu().numpy()
+    assert np.array_equal(np.isfinite(gv), np.isfinite(ev))
+    assert rel_err(gv[np.isfinite(ev)], ev[np.isfinite(ev)]) <= TOL["bf16"]
+    assert np.array_equal(kr.float().cpu().numpy(), ekr.astype(np.float32), equal_nan=True)
+
+
 def test_gqa_path_uses_matrix_cores_at_gqla_shapes():
     for sq in (1, 2):
         cfg = get_config("gqla-b32-t8192", s_q=sq)
