@@ -163,7 +163,9 @@ __global__ __launch_bounds__(256, 1) void expand_mfma_kernel(
   // the end of half h: this wave's loads of half h + 1 have landed (the instructions issued
   // after them, in order: the 4 output stores of half h - 1 when h > 0, group 0's key store,
   // the 9 loads of half h + 2 when there is one; the key store is left out of the count,
-  // which only makes the wait cover it too), its output staging too; then the barrier
+  // which only makes the wait cover it too), its output staging too; then the barrier.
+  // The counts assume no vector-memory instructions of the compiler's own in the loop: the
+  // kernel uses no scratch (a spill's scratch accesses would count here too).
   auto end_half = [&](int h) {
     if (h + 1 >= n_half)
       wait_vm_lgkm0<63>();
