@@ -125,6 +125,12 @@ def test_tiny_f32_ragged_mtp_and_empty_rows():
     check_absorbed_all_steps(make_inputs(cfg, seed=1), S=5)
 
 
+def test_tiny_f32_zero_length_sequences():
+    """Sequences with no cached token at all (every chunk empty): out = 0, lse = -inf."""
+    cfg = get_config("tiny-f32", batch=4, s_q=2, ctx=("list", [0, 65, 0, 30]))
+    check_absorbed_all_steps(make_inputs(cfg, seed=5), S=3)
+
+
 def test_tiny_f32_step_entry_point_matches_steps():
     inp = make_inputs(get_config("tiny-f32"))
     d = DeviceInputs(inp)
@@ -144,16 +150,18 @@ def test_tiny_f32_step_entry_point_matches_steps():
     ("dsv2-b16-t4096", 2, [1 + (97 * i) % 300 for i in range(20)], 3),
     ("dsv2-b16-t4096", 1, [5000, 64], 64),
     ("dsv2-b16-t4096", 2, [1, 2, 130], 1),
+    ("dsv2-b16-t4096", 1, [0, 577, 0, 64], 4),
     ("gqla-b32-t8192", 2, [700, 64, 1999], 5),
+    ("gqla-b32-t8192", 1, [0, 700, 0], 3),
     ("gqla-shard-b32-t65536", 1, [700, 64, 1999], 3),
 ])
 def test_bf16_step_entry_point_matches_steps(name, s_q, ctx, S):
     """At bf16 with d_c 512 and d_v 128 the step entry point merges the splits and
     up-projects in one kernel; its outputs must equal those of the separate entry points
     bit for bit (20 sequences at s_q = 2 give two query blocks of 32, the second ragged;
-    s_q = 2 over one token gives rows with no visible token; the 32- and 4-head shapes have
-    too few workgroups for the fused kernel and take the separate kernels inside the step),
-    and match the oracle."""
+    s_q = 2 over one token gives rows with no visible token, and sequences of length 0 give
+    whole sequences of empty chunks; the 32- and 4-head shapes have too few workgroups for
+    the fused kernel and take the separate kernels inside the step), and match the oracle."""
     cfg = get_config(name, batch=len(ctx), s_q=s_q, ctx=("list", ctx))
     inp = make_inputs(cfg, seed=21)
     announce(f"case {name} s_q={s_q} ctx={ctx[:6]} S={S}")
@@ -362,6 +370,7 @@ def expanded_pools(d):
 @pytest.mark.parametrize("dtype,ctx,S", [("f32", [300, 64, 1], 3), ("bf16", [1000, 129], 2),
                                          ("bf16", [4096, 2000], 4),
                                          ("bf16", [1, 33, 64, 65, 95], 8),
+                                         ("bf16", [0, 700, 0, 65], 3),
                                          ("shard", [1, 700, 2049], 5),
                                          ("mtp", [1, 2, 130, 1999], 3)])
 def test_gqla_expand_and_gqa_path(dtype, ctx, S):
