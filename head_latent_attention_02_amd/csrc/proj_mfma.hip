@@ -36,11 +36,15 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPM = 64;      // weight rows per workgroup
 constexpr int kPK = 256;     // K per tile
-constexpr int kPN = 32;      // tokens per workgroup (grid z covers more)
+constexpr int kPN = 32;      // tokens per matrix-core block
+constexpr int kPNB = 4;      // token blocks per workgroup: 128 tokens (grid z covers more)
 
 struct ProjSmem {
-  u32x4 w[2][kPM * kPK / 8];  // two weight tiles, 16-byte chunks (64 KB)
-  float part[2][64 * 16];     // the K-half-1 partial sums of the two row blocks
+  union {
+    u32x4 w[2][kPM * kPK / 8];        // two weight tiles, 16-byte chunks (64 KB)
+    float part[kPNB][2][64 * 16];     // after the last tile: the K-half-1 partial sums of
+                                      // each token block's two row blocks (32 KB)
+  };
 };
 
 // chunk ch (of 32) of tile row r sits at chunk ch ^ (r & 15): the operand reads take one
@@ -50,14 +54,17 @@ __device__ __forceinline__ int pswz(int r, int ch) { return ch ^ (r & 15); }
 __device__ __forceinline__ bf16x8 load_x8(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
+// fp32 token rows (the output projections' input) are rounded to bf16 for the matrix cores,
+// to nearest even, two per v_cvt_pk_bf16_f32: a software rounding cost ~5 VALU instructions
+// per value here, more than the tile's MFMAs
 __device__ __forceinline__ bf16x8 load_x8(const float* p) {
   const float4 a = *reinterpret_cast<const float4*>(p);
   const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  const uint32_t u0 = f32_to_bf16(a.x) | (static_cast<uint32_t>(f32_to_bf16(a.y)) << 16);
-  const uint32_t u1 = f32_to_bf16(a.z) | (static_cast<uint32_t>(f32_to_bf16(a.w)) << 16);
-  const uint32_t u2 = f32_to_bf16(b.x) | (static_cast<uint32_t>(f32_to_bf16(b.y)) << 16);
-  const uint32_t u3 = f32_to_bf16(b.z) | (static_cast<uint32_t>(f32_to_bf16(b.w)) << 16);
-  return __builtin_bit_cast(bf16x8, (u32x4){u0, u1, u2, u3});
+  const bf16x8 v = {static_cast<__bf16>(a.x), static_cast<__bf16>(a.y),
+                    static_cast<__bf16>(a.z), static_cast<__bf16>(a.w),
+                    static_cast<__bf16>(b.x), static_cast<__bf16>(b.y),
+                    static_cast<__bf16>(b.z), static_cast<__bf16>(b.w)};
+  return v;
 }
 
 template <typename XT, typename OT, bool ATOMIC>
@@ -69,7 +76,9 @@ __global__ __launch_bounds__(256, 2) void proj_mfma_kernel(
   const int m0 = blockIdx.x * kPM;
   const int ka = blockIdx.y * k_split;
   const int kb = min(ka + k_split, K);
-  const int n0 = blockIdx.z * kPN;
+  // up to kPNB blocks of 32 tokens, so the weights stream once for up to 128 tokens
+  const int n0 = blockIdx.z * kPN * kPNB;
+  const int nbc = min(kPNB, (N - n0 + kPN - 1) / kPN);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n32 = lane & 31, g = lane >> 5;
   const int rb = wave & 1, kh = wave >> 1;
@@ -92,10 +101,9 @@ __global__ __launch_bounds__(256, 2) void proj_mfma_kernel(
       sm.w[buf][r * 32 + pswz(r, ch)] = stg[j];
     }
   };
-  const int n = n0 + n32;
-  const bool n_ok = n < N;
-  const XT* xrow = X + static_cast<size_t>(n_ok ? n : 0) * K;
-  f32x16 acc = {};
+  f32x16 acc[kPNB];
+#pragma unroll
+  for (int nb = 0; nb < kPNB; ++nb) acc[nb] = f32x16{};
   if (n_tiles > 0) {
     load_tile(0);
     store_tile(0);
@@ -104,18 +112,28 @@ __global__ __launch_bounds__(256, 2) void proj_mfma_kernel(
     for (int t = 0; t < n_tiles; ++t) {
       const int buf = t & 1;
       const int k0 = ka + t * kPK;
-      // the wave's 8 K-steps of this tile: A = weight rows 32 rb + n32, B = token n
+      // the wave's 8 K-steps of this tile: A = weight rows 32 rb + n32, B = token
+      // n0 + 32 nb + n32 of each token block
       const int r = 32 * rb + n32;
-      bf16x8 a[8], b[8];
+      bf16x8 a[8];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int ks = 8 * kh + s;
         a[s] = __builtin_bit_cast(bf16x8, sm.w[buf][r * 32 + pswz(r, 2 * ks + g)]);
-        b[s] = n_ok ? load_x8(xrow + k0 + 16 * ks + 8 * g) : bf16x8{};
       }
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b[s], acc, 0, 0, 0);
+      for (int nb = 0; nb < kPNB; ++nb) {
+        if (nb < nbc) {
+          const int n = n0 + kPN * nb + n32;
+          const XT* xrow = X + static_cast<size_t>(n < N ? n : 0) * K + k0 + 8 * g;
+          bf16x8 b[8];
+#pragma unroll
+          for (int s = 0; s < 8; ++s) b[s] = n < N ? load_x8(xrow + 16 * (8 * kh + s)) : bf16x8{};
+#pragma unroll
+          for (int s = 0; s < 8; ++s)
+            acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b[s], acc[nb], 0, 0, 0);
+        }
+      }
       if (t + 1 < n_tiles) {
         store_tile(buf ^ 1);          // its last readers finished before the last barrier
         if (t + 2 < n_tiles) load_tile(t + 2);
@@ -123,44 +141,54 @@ __global__ __launch_bounds__(256, 2) void proj_mfma_kernel(
       __syncthreads();
     }
   }
-  // add the K-half-1 partials of each row block
+  // add the K-half-1 partials of each row block (the weight tiles' LDS is free: every wave
+  // passed the last tile's barrier)
   if (kh == 1) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sm.part[rb][i * 64 + lane] = acc[i];
+    for (int nb = 0; nb < kPNB; ++nb)
+      if (nb < nbc) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sm.part[nb][rb][i * 64 + lane] = acc[nb][i];
+      }
   }
   __syncthreads();
   if (kh == 1) return;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] += sm.part[rb][i * 64 + lane];
-  if (!n_ok) return;
   // lane holds token n, rows m0 + 32 rb + 8 (i / 4) + 4 g + i % 4
   const int mb = m0 + 32 * rb + 4 * g;
-  if (rope_dim > 0) {
-    const int b_ = n / s_q, s_ = n - b_ * s_q;
-    const double pos = static_cast<double>(lens[b_] - s_q + s_);
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const int m = mb + 8 * (i >> 2) + (i & 3);
-      const int rr = m % block_dim - lat_dim;
-      if (rr >= 0) {                  // an even RoPE row and its partner m + 1
-        const double ang = pos * exp(-log_base * static_cast<double>(rr) / rope_dim);
-        const float c = static_cast<float>(cos(ang)), sn = static_cast<float>(sin(ang));
-        const float x0 = acc[i], x1 = acc[i + 1];
-        acc[i] = x0 * c - x1 * sn;
-        acc[i + 1] = x0 * sn + x1 * c;
+  for (int nb = 0; nb < kPNB; ++nb) {
+    const int n = n0 + kPN * nb + n32;
+    if (nb >= nbc || n >= N) continue;
+    f32x16 v = acc[nb];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] += sm.part[nb][rb][i * 64 + lane];
+    if (rope_dim > 0) {
+      const int b_ = n / s_q, s_ = n - b_ * s_q;
+      const double pos = static_cast<double>(lens[b_] - s_q + s_);
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const int m = mb + 8 * (i >> 2) + (i & 3);
+        const int rr = m % block_dim - lat_dim;
+        if (rr >= 0) {                  // an even RoPE row and its partner m + 1
+          const double ang = pos * exp(-log_base * static_cast<double>(rr) / rope_dim);
+          const float c = static_cast<float>(cos(ang)), sn = static_cast<float>(sin(ang));
+          const float x0 = v[i], x1 = v[i + 1];
+          v[i] = x0 * c - x1 * sn;
+          v[i + 1] = x0 * sn + x1 * c;
+        }
       }
     }
-  }
-  OT* crow = C + static_cast<size_t>(n) * ldc;
+    OT* crow = C + static_cast<size_t>(n) * ldc;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int m = mb + 8 * q;
-    if constexpr (ATOMIC) {
+    for (int q = 0; q < 4; ++q) {
+      const int m = mb + 8 * q;
+      if constexpr (ATOMIC) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(crow + m + e, acc[4 * q + e]);
-    } else {
+        for (int e = 0; e < 4; ++e) atomicAdd(crow + m + e, v[4 * q + e]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) stf(crow + m + e, acc[4 * q + e]);
+        for (int e = 0; e < 4; ++e) stf(crow + m + e, v[4 * q + e]);
+      }
     }
   }
 }
@@ -247,14 +275,17 @@ __global__ void zero_f32_kernel(float* p, size_t n) {
 }
 
 // C = W X^T for M rows of W, K wide, N token rows; splits K over workgroups (fp32 atomics
-// into a zeroed C) when 64-row blocks alone give fewer than ~1024 workgroups.
+// into a zeroed C) when 64-row blocks alone give fewer than ~1024 workgroups, at most
+// 512 / N splits.
 template <typename XT, typename OT>
 hipError_t launch_proj(const bf16_t* W, int M, int K, const XT* X, int N, OT* C, int ldc,
                        int block_dim, int lat_dim, int rope_dim, const int32_t* lens, int s_q,
                        double log_base, hipStream_t st) {
-  const int m_blocks = M / kPM, n_blocks = (N + kPN - 1) / kPN;
+  const int m_blocks = M / kPM, n_blocks = (N + kPN * kPNB - 1) / (kPN * kPNB);
   int splits = (1024 + m_blocks * n_blocks - 1) / (m_blocks * n_blocks);
   splits = max(1, min(splits, K / kPK));
+  // every split adds N x M partial sums with atomics: keep splits x N within 512 x M
+  splits = max(1, min(splits, 512 / max(N, 1)));
   if constexpr (!std::is_same<OT, float>::value) splits = 1;   // bf16 outputs: no atomics
   if (rope_dim > 0) splits = 1;                                 // rotate complete sums only
   const int k_split = ((K / kPK + splits - 1) / splits) * kPK;

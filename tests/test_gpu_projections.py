@@ -40,9 +40,13 @@ def setup(name, d_model, **kw):
 CASES = [("dsv2-b16-t4096", 512, dict(batch=2, ctx=("list", [300, 129]))),
          ("gqla-b32-t8192", 512, dict(batch=3, ctx=("list", [700, 65, 1]))),
          ("mtp-b64-ragged", 256, dict(batch=2, ctx=("list", [130, 64])))]
+# more tokens than one matrix-core block of 32: 80 tokens (three blocks, the last partial)
+# and 140 tokens (a second workgroup of token blocks, 12 tokens in it)
+MANY = [("mtp-b64-ragged", 256, dict(batch=40, ctx=("list", [130 + 7 * i for i in range(40)]))),
+        ("dsv2-b16-t4096", 256, dict(batch=140, ctx=("list", [64 + i for i in range(140)])))]
 
 
-@pytest.mark.parametrize("name,d_model,kw", CASES)
+@pytest.mark.parametrize("name,d_model,kw", CASES + MANY)
 def test_query_projection_unfolded_and_folded(name, d_model, kw):
     cfg, inp, pr, d, dev = setup(name, d_model, **kw)
     print(f"case {name} d_model={d_model} B={cfg.batch} s_q={cfg.s_q}", flush=True)
@@ -69,7 +73,7 @@ def test_query_projection_unfolded_and_folded(name, d_model, kw):
     assert max(e_q, e_w, e_abs, e_def) <= TOL
 
 
-@pytest.mark.parametrize("name,d_model,kw", CASES)
+@pytest.mark.parametrize("name,d_model,kw", CASES + MANY)
 def test_output_projection_unfolded_and_folded(name, d_model, kw):
     cfg, inp, pr, d, dev = setup(name, d_model, **kw)
     B, s_q, H = cfg.batch, cfg.s_q, cfg.n_heads
