@@ -545,7 +545,7 @@ def main():
     global FLUSH_KIND
     FLUSH_KIND = args.flush
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the "
               "decode path has no multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
