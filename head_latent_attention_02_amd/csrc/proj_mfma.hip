@@ -269,6 +269,155 @@ __global__ __launch_bounds__(256) void fold_o_kernel(const bf16_t* __restrict__ 
                             static_cast<size_t>(h) * d_c + c8) = o;
 }
 
+// More than 32 token rows: a matrix-product tiling instead of the weight stream above.  The
+// stream reads every token row once per 64 weight rows, which from 128 tokens on moves four
+// times the weight bytes through each CU; here a workgroup takes 256 weight rows x 128
+// tokens, K in steps of 64, with both operands staged through LDS (double-buffered, 96 KB),
+// so the token rows are read once per 256 weight rows.  Wave w: weight rows 64 w .. +64 (two
+// 32-row blocks) x the 128 tokens (four 32-token blocks), eight accumulators.
+constexpr int kGM = 256;     // weight rows per workgroup
+constexpr int kGN = 128;     // tokens per workgroup
+constexpr int kGK = 64;      // K per tile
+
+struct GemmSmem {
+  u32x4 a[2][kGM * kGK / 8];  // weight tiles [row][8 chunks of 8 bf16] (2 x 32 KB)
+  u32x4 b[2][kGN * kGK / 8];  // token tiles, the same layout (2 x 16 KB)
+};
+
+// chunk c of row r sits at chunk c ^ ((r >> 1) & 7): a 128-byte row covers half the banks,
+// so rows r and r ^ 1 use the two halves and the swizzle spreads 16 rows over all of them
+__device__ __forceinline__ int gswz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+__device__ __forceinline__ u32x4 pack_x8(const bf16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 pack_x8(const float* p) {
+  return __builtin_bit_cast(u32x4, load_x8(p));
+}
+
+template <typename XT, typename OT, bool ATOMIC>
+__global__ __launch_bounds__(256, 1) void proj_gemm_kernel(
+    const bf16_t* __restrict__ W, int M, int K, const XT* __restrict__ X, int N,
+    OT* __restrict__ C, int ldc, int k_split, int block_dim, int lat_dim, int rope_dim,
+    const int32_t* __restrict__ lens, int s_q, double log_base) {
+  __shared__ __attribute__((aligned(16))) GemmSmem sm;
+  const int m0 = blockIdx.x * kGM;
+  const int ka = blockIdx.y * k_split;
+  const int kb = min(ka + k_split, K);
+  const int n0 = blockIdx.z * kGN;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n32 = lane & 31, g = lane >> 5;
+  const int n_tiles = (kb - ka) / kGK;
+  // staging: weight chunk j of a thread is row (tid + 256 j) / 8, chunk tid % 8 (eight
+  // threads read a row's 128 contiguous bytes); token chunks the same, four per thread
+  u32x4 sa[8], sb[4];
+  auto load_tile = [&](int t) {
+    const int k0 = ka + t * kGK;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int f = tid + 256 * j, r = f >> 3, c = f & 7;
+      sa[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          W + static_cast<size_t>(m0 + r) * K + k0 + 8 * c));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int f = tid + 256 * j, r = f >> 3, c = f & 7;
+      const int n = n0 + r;
+      sb[j] = n < N ? pack_x8(X + static_cast<size_t>(n) * K + k0 + 8 * c) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int f = tid + 256 * j, r = f >> 3, c = f & 7;
+      sm.a[buf][r * 8 + gswz(r, c)] = sa[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int f = tid + 256 * j, r = f >> 3, c = f & 7;
+      sm.b[buf][r * 8 + gswz(r, c)] = sb[j];
+    }
+  };
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) acc[rb][tb] = f32x16{};
+  load_tile(0);
+  store_tile(0);
+  if (n_tiles > 1) load_tile(1);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    // four K-steps of 16: A = weight row 64 wave + 32 rb + n32, B = token 32 tb + n32, both
+    // 8 values at K offset 16 s + 8 g (chunk 2 s + g)
+#pragma unroll
+    for (int s = 0; s < kGK / 16; ++s) {
+      bf16x8 a[2], b[4];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int r = 64 * wave + 32 * rb + n32;
+        a[rb] = __builtin_bit_cast(bf16x8, sm.a[buf][r * 8 + gswz(r, 2 * s + g)]);
+      }
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const int r = 32 * tb + n32;
+        b[tb] = __builtin_bit_cast(bf16x8, sm.b[buf][r * 8 + gswz(r, 2 * s + g)]);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b[tb], acc[rb][tb], 0, 0, 0);
+    }
+    if (t + 1 < n_tiles) {
+      store_tile(buf ^ 1);          // its last readers finished before the last barrier
+      if (t + 2 < n_tiles) load_tile(t + 2);
+    }
+    __syncthreads();
+  }
+  // lane holds token 32 tb + n32 of the block, rows m0 + 64 wave + 32 rb + 8 (i / 4) + 4 g
+  // + i % 4
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int n = n0 + 32 * tb + n32;
+    if (n >= N) continue;
+    OT* crow = C + static_cast<size_t>(n) * ldc;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      f32x16 v = acc[rb][tb];
+      const int mb = m0 + 64 * wave + 32 * rb + 4 * g;
+      if (rope_dim > 0) {
+        const int b_ = n / s_q, s_ = n - b_ * s_q;
+        const double pos = static_cast<double>(lens[b_] - s_q + s_);
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const int m = mb + 8 * (i >> 2) + (i & 3);
+          const int rr = m % block_dim - lat_dim;
+          if (rr >= 0) {                  // an even RoPE row and its partner m + 1
+            const double ang = pos * exp(-log_base * static_cast<double>(rr) / rope_dim);
+            const float c = static_cast<float>(cos(ang)), sn = static_cast<float>(sin(ang));
+            const float x0 = v[i], x1 = v[i + 1];
+            v[i] = x0 * c - x1 * sn;
+            v[i + 1] = x0 * sn + x1 * c;
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = mb + 8 * q;
+        if constexpr (ATOMIC) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) atomicAdd(crow + m + e, v[4 * q + e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) stf(crow + m + e, v[4 * q + e]);
+        }
+      }
+    }
+  }
+}
+
 __global__ void zero_f32_kernel(float* p, size_t n) {
   const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i < n) p[i] = 0.f;
@@ -281,6 +430,29 @@ template <typename XT, typename OT>
 hipError_t launch_proj(const bf16_t* W, int M, int K, const XT* X, int N, OT* C, int ldc,
                        int block_dim, int lat_dim, int rope_dim, const int32_t* lens, int s_q,
                        double log_base, hipStream_t st) {
+  if (N > kPN && M % kGM == 0 && K % kGK == 0) {
+    const int gm = M / kGM, gn = (N + kGN - 1) / kGN;
+    int gs = (256 + gm * gn - 1) / (gm * gn);             // about one workgroup per CU
+    gs = max(1, min(gs, min(K / kGK, 512 / N)));
+    if constexpr (!std::is_same<OT, float>::value) gs = 1;
+    if (rope_dim > 0) gs = 1;
+    const int ks = ((K / kGK + gs - 1) / gs) * kGK;
+    gs = (K + ks - 1) / ks;
+    const dim3 grid(gm, gs, gn);
+    if (gs > 1) {
+      if constexpr (std::is_same<OT, float>::value) {
+        const size_t n = static_cast<size_t>(N) * ldc;
+        hipLaunchKernelGGL(zero_f32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
+                           dim3(256), 0, st, C, n);
+        hipLaunchKernelGGL((proj_gemm_kernel<XT, OT, true>), grid, dim3(256), 0, st, W, M, K, X,
+                           N, C, ldc, ks, block_dim, lat_dim, rope_dim, lens, s_q, log_base);
+      }
+    } else {
+      hipLaunchKernelGGL((proj_gemm_kernel<XT, OT, false>), grid, dim3(256), 0, st, W, M, K, X,
+                         N, C, ldc, ks, block_dim, lat_dim, rope_dim, lens, s_q, log_base);
+    }
+    return hipGetLastError();
+  }
   const int m_blocks = M / kPM, n_blocks = (N + kPN * kPNB - 1) / (kPN * kPNB);
   int splits = (1024 + m_blocks * n_blocks - 1) / (m_blocks * n_blocks);
   splits = max(1, min(splits, K / kPK));
