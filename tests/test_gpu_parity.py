@@ -535,7 +535,10 @@ def test_full_dsv2_b16_t4096():
 
 
 def test_full_long_b4_t131072():
-    sampled_full_check(get_config("long-b4-t131072"), [0, 1, 2, 3], [0, 127, 45, 90])
+    # ten heads per sequence: rows of both score waves of both 64-row blocks, each block's
+    # first and last row
+    sampled_full_check(get_config("long-b4-t131072"), [0, 1, 2, 3],
+                       [0, 13, 31, 45, 63, 64, 77, 90, 101, 127])
 
 
 def test_full_gqla_b32_t65536_absorbed():
