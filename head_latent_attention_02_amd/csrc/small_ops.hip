@@ -610,44 +610,51 @@ __global__ __launch_bounds__(64 * kUvmWaves) void out_uv_mfma_kernel(
 
 // ---------------------------------------------------------------- a3 + a4 fused
 // The step's split merge and value up-projection in one launch (bf16 weights, d_c = 512,
-// d_v = 128, at most 64 splits, heads a multiple of 8).  Block (head h, half of its 128
-// value rows, 32 queries), 8 waves; the two halves of a head are 8 blocks apart, so they
-// run on one XCD and the second one's partial reads hit its L2.  Arithmetic is the
-// same, operation for operation, as combine_kernel followed by out_uv_mfma_kernel, so the
-// results are bitwise those of the two separate entry points; what changes is that the
-// merged latent rows go to the up-projection through LDS and that the weight loads, the
-// partial loads and the lse reductions are all in flight together.
-//   wave w: value rows 64 half + 32 (w % 2) .. +32 and latent quarter w / 2 of the
-//   up-projection; all waves share the merge (4 queries x 512 columns per pass), which
-//   both halves compute (only half 0 stores o_lat and lse).
+// d_v = 128, at most 64 splits, heads a multiple of 8).  Block (head h, NV of its four
+// 32-row value blocks, 32 queries), 4 NV waves.  Arithmetic is the same, operation for
+// operation, as combine_kernel followed by out_uv_mfma_kernel, so the results are bitwise
+// those of the two separate entry points; what changes is that the merged latent rows go to
+// the up-projection through LDS and that the weight loads, the partial loads and the lse
+// reductions are all in flight together.
+//   wave w: value rows 32 (NV half + w % NV) .. +32 and latent quarter w / NV of the
+//   up-projection; all waves share the merge (one query x 512 columns per 128 threads and
+//   pass).
+//   NV = 2: a head's two halves are 8 blocks apart, so they run on one XCD and the second
+//   one's partial reads hit its L2; both compute the merge (only half 0 stores o_lat and
+//   lse).  NV = 4: one block per head and query block reads each partial once, which halves
+//   the bytes each CU pulls; used when heads x query blocks alone fill the CUs.
 constexpr int kFuQ = 32;          // queries per block
-constexpr int kFuBatch = 32;      // partial loads per thread in flight at once
 constexpr int kFuRow = 512 + 8;   // bf16 elements per LDS row of merged latents (padded)
 
-__global__ __launch_bounds__(512) void combine_out_uv_kernel(
+template <int NV>
+__global__ __launch_bounds__(256 * NV) void combine_out_uv_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part,
     const bf16_t* __restrict__ w_uv, float* __restrict__ o_lat, float* __restrict__ lse,
     float* __restrict__ out, int NQ, int H, int Hw, int S) {
   constexpr int d_c = 512, d_v = 128;
+  constexpr int kWaves = 4 * NV, kPass = 2 * NV;   // waves; queries merged per pass
+  // partial loads per thread in flight at once (1024 threads leave 128 VGPRs a thread)
+  constexpr int kFuBatch = NV == 2 ? 32 : 8;
   __shared__ __align__(16) bf16_t ob[kFuQ * kFuRow];   // merged latents as MFMA B rows
   __shared__ float wts[kFuQ][64];                       // chunk weights e^{lse_u - max}
   __shared__ float inv_s[kFuQ];
-  __shared__ float red[2][3][16][64];                   // quarters 1-3 per value block
+  __shared__ float red[NV][3][16][64];                  // quarters 1-3 per value block
   const int hx = blockIdx.x;
-  const int h = (hx >> 4) * 8 + (hx & 7), half = (hx >> 3) & 1;
+  const int h = NV == 2 ? (hx >> 4) * 8 + (hx & 7) : hx;
+  const int half = NV == 2 ? (hx >> 3) & 1 : 0;
   const int q0 = blockIdx.y * kFuQ;
   const int nqb = min(kFuQ, NQ - q0);
   const int w = h / (H / Hw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m = lane & 31, g = lane >> 5, vb = wave & 1, kq = wave >> 1;
-  const int v0 = 64 * half + 32 * vb;   // this wave's first value row
+  const int m = lane & 31, g = lane >> 5, vb = wave % NV, kq = wave / NV;
+  const int v0 = 32 * (NV * half + vb);   // this wave's first value row
 
   // (0) the chunk lse of this wave's queries (step 3), loaded first: loads complete in
   // issue order, so step 3 then waits for these alone, not for the weights and partials
-  float lq[kFuQ / 8];
+  float lq[kFuQ / kWaves];
 #pragma unroll
-  for (int i = 0; i < kFuQ / 8; ++i) {
-    const int n = wave + 8 * i;
+  for (int i = 0; i < kFuQ / kWaves; ++i) {
+    const int n = wave + kWaves * i;
     lq[i] = (n < nqb && lane < S) ? lse_part[(static_cast<size_t>(q0 + n) * H + h) * S + lane]
                                   : -INFINITY;
   }
@@ -671,8 +678,8 @@ __global__ __launch_bounds__(512) void combine_out_uv_kernel(
   if (cq < nqb) issue(cq, 0);
   // (3) chunk weights, 1 / sum and lse of every query: one wave per query, lane = split
 #pragma unroll
-  for (int i = 0; i < kFuQ / 8; ++i) {
-    const int n = wave + 8 * i;
+  for (int i = 0; i < kFuQ / kWaves; ++i) {
+    const int n = wave + kWaves * i;
     const float l = lq[i];
     float mx = l;
 #pragma unroll
@@ -696,8 +703,8 @@ __global__ __launch_bounds__(512) void combine_out_uv_kernel(
     if (lane == 0) inv_s[n] = inv;
   }
   __syncthreads();
-  // (4) merge, 4 queries x 512 columns per pass; rows past the block's queries are zeros
-  for (int n = cq; n < kFuQ; n += 4) {
+  // (4) merge, kPass queries x 512 columns per pass; rows past the block's queries are zeros
+  for (int n = cq; n < kFuQ; n += kPass) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (n < nqb) {
       for (int u0 = 0; u0 < S; u0 += kFuBatch) {
@@ -926,24 +933,33 @@ hipError_t launch_out_uv(const mla_shape_t& s, const float* o_lat, const void* w
   return hipGetLastError();
 }
 
-bool combine_out_uv_supported(const mla_shape_t& s) {
-  // The fused kernel runs 2 H ceil(B s_q / 32) workgroups.  Below one per CU the separate
-  // kernels, which spread the merge over B s_q H workgroups, are faster (32 heads x 32
-  // queries: 17.2 us fused against 5.9 + 6.0 us; 128 heads x 4 queries: 13.9 against 9.9 +
-  // 8.2 us).
+// Workgroups of the fused kernel with whole heads (NV = 4) and with half heads (NV = 2).
+static int64_t fused_blocks(const mla_shape_t& s, int nv) {
   const int64_t nq = static_cast<int64_t>(s.batch) * s.s_q;
-  const int64_t wgs = 2 * static_cast<int64_t>(s.n_heads) * ((nq + kFuQ - 1) / kFuQ);
+  return (4 / nv) * static_cast<int64_t>(s.n_heads) * ((nq + kFuQ - 1) / kFuQ);
+}
+
+bool combine_out_uv_supported(const mla_shape_t& s) {
+  // Below one workgroup per CU the separate kernels, which spread the merge over
+  // B s_q H workgroups, are faster (32 heads x 32 queries: 17.2 us fused against 5.9 +
+  // 6.0 us; 128 heads x 4 queries: 13.9 against 9.9 + 8.2 us).
   return s.dtype == MLA_BF16 && s.d_c == 512 && s.d_v == 128 && s.n_splits <= 64 &&
-         s.n_heads % 8 == 0 && wgs >= 256;
+         s.n_heads % 8 == 0 && fused_blocks(s, 2) >= 256;
 }
 
 hipError_t launch_combine_out_uv(const mla_shape_t& s, const float* o_part,
                                  const float* lse_part, const void* w_uv, float* o_lat,
                                  float* lse, float* out, hipStream_t st) {
   const int NQ = s.batch * s.s_q;
-  hipLaunchKernelGGL(combine_out_uv_kernel, dim3(2 * s.n_heads, (NQ + kFuQ - 1) / kFuQ),
-                     dim3(512), 0, st, o_part, lse_part, static_cast<const bf16_t*>(w_uv), o_lat, lse,
-                     out, NQ, s.n_heads, s.n_wheads, s.n_splits);
+  const dim3 qb(1, (NQ + kFuQ - 1) / kFuQ);
+  if (fused_blocks(s, 4) >= 256)
+    hipLaunchKernelGGL(combine_out_uv_kernel<4>, dim3(s.n_heads, qb.y), dim3(1024), 0, st,
+                       o_part, lse_part, static_cast<const bf16_t*>(w_uv), o_lat, lse, out, NQ,
+                       s.n_heads, s.n_wheads, s.n_splits);
+  else
+    hipLaunchKernelGGL(combine_out_uv_kernel<2>, dim3(2 * s.n_heads, qb.y), dim3(512), 0, st,
+                       o_part, lse_part, static_cast<const bf16_t*>(w_uv), o_lat, lse, out, NQ,
+                       s.n_heads, s.n_wheads, s.n_splits);
   return hipGetLastError();
 }
 
