@@ -170,6 +170,23 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const T* __restrict__ q,
   }
 }
 
+// q_abs[q, h, d_c : d_c + d_r] = q[q, h, d_n : d_n + d_r] for the block's queries, in 16-byte
+// chunks (d_r is a multiple of 8), shared by the gridDim.y column blocks of head h: at the
+// supported shapes each thread copies at most one chunk (one load, one store).
+__device__ __forceinline__ void copy_rope_part(const bf16_t* __restrict__ q,
+                                               bf16_t* __restrict__ q_abs, int q0, int nq,
+                                               int H, int h, int d_n, int d_r, int d_c) {
+  const int per_q = d_r / 8, chunks = nq * per_q;
+  const int part = (chunks + gridDim.y - 1) / gridDim.y;
+  const int c_lo = blockIdx.y * part, c_hi = min(chunks, c_lo + part);
+  for (int i = c_lo + threadIdx.x; i < c_hi; i += blockDim.x) {
+    const int jq = i / per_q, r8 = i - jq * per_q;
+    const size_t qrow = static_cast<size_t>(q0 + jq) * H + h;
+    *reinterpret_cast<uint4*>(q_abs + qrow * (d_c + d_r) + d_c + 8 * r8) =
+        *reinterpret_cast<const uint4*>(q + qrow * (d_n + d_r) + d_n + 8 * r8);
+  }
+}
+
 // a1 for a few bf16 queries (at most 8 per block), the weight read streamed at full width.
 // Block (head h, 256 latent columns c0 .., QB queries), 256 threads, one block per CU at 128
 // heads.  Lane l of wave wv owns columns c0 + 8 (l % 32) .. +8 and the weight rows
@@ -268,13 +285,7 @@ __global__ __launch_bounds__(256) void absorb_q_stream_kernel(const bf16_t* __re
     const float v = ((red[0][k][c] + red[1][k][c]) + red[2][k][c]) + red[3][k][c];
     q_abs[(static_cast<size_t>(q0 + k) * H + h) * D + c0 + c] = f32_to_bf16(v);
   }
-  if (blockIdx.y == 0) {
-    for (int idx = tid; idx < nq * d_r; idx += 256) {
-      const int k = idx / d_r, r = idx - k * d_r;
-      const size_t qrow = static_cast<size_t>(q0 + k) * H + h;
-      q_abs[qrow * D + d_c + r] = q[qrow * dq + d_n + r];
-    }
-  }
+  copy_rope_part(q, q_abs, q0, nq, H, h, d_n, d_r, d_c);
 }
 
 // a1 on the matrix cores (bf16, d_n = 128, 16 or more queries).  Block (head h, 128 latent
@@ -370,13 +381,7 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(const bf16_t* __rest
       *reinterpret_cast<uint2*>(orow + 8 * jg) = make_uint2(pk[0], pk[1]);
     }
   }
-  if (blockIdx.y == 0) {
-    for (int idx = tid; idx < nq * d_r; idx += 256) {
-      const int jq = idx / d_r, r = idx - jq * d_r;
-      const size_t qrow = static_cast<size_t>(q0 + jq) * H + h;
-      q_abs[qrow * D + d_c + r] = q[qrow * dq + d_n + r];
-    }
-  }
+  copy_rope_part(q, q_abs, q0, nq, H, h, d_n, d_r, d_c);
 }
 
 // ---------------------------------------------------------------- a3 combine
