@@ -289,8 +289,9 @@ __global__ __launch_bounds__(256) void absorb_q_stream_kernel(const bf16_t* __re
 }
 
 // a1 on the matrix cores (bf16, d_n = 128, 16 or more queries).  Block (head h, 128 latent
-// columns c0 .., 32 NB queries q0 ..), 4 waves; wave w computes q_abs^T[c0 + 32 w + m][q] =
-// sum_i W_UK[h][i][c] q[q][i] with v_mfma_f32_32x32x16_bf16: the weight slice, staged once in
+// columns c0 .., 32 NB queries q0 ..), 4 waves; wave w computes q_abs^T[c][q] =
+// sum_i W_UK[h][i][c] q[q][i] for the 32 queries of query block w % NB and NB column blocks
+// of 32, with v_mfma_f32_32x32x16_bf16: the weight slice, staged once in
 // LDS (rows of 256 bytes, 16-byte chunks XOR-swizzled by row), is the A operand, read
 // transposed with ds_read_b64_tr_b16; the queries' no-position parts are the B operand,
 // 16-byte loads in their natural layout.  Each weight byte is read once per 32 NB queries
@@ -313,6 +314,9 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(const bf16_t* __rest
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n32 = lane & 31, g = lane >> 5;
   const int nq = min(32 * NB, NQ - q0);
+  // wave w: the 32 queries of query block w % NB and the NB column blocks of 32 starting at
+  // block (w / NB) NB of the block's 128 columns, so each wave loads one query block only
+  const int qblk = wave % NB, cb0 = (wave / NB) * NB;
   // weight slice W_UK[wh][0:128][c0:c0+128]: 2048 chunks of 16 bytes, 8 per thread
   const bf16_t* W = w_uk + static_cast<size_t>(wh) * d_n * d_c + c0;
   uint4 wv[8];
@@ -321,16 +325,15 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(const bf16_t* __rest
     const int idx = tid + 256 * k, i = idx >> 4, ch = idx & 15;
     wv[k] = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(i) * d_c + 8 * ch);
   }
-  // B operands: query 32 nb + n32, rows i = 16 kt + 8 g .. +8 (zeros past the last query)
-  bf16x8_t qb[NB][8];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int qi = 32 * nb + n32;
+  // B operands: query 32 qblk + n32, rows i = 16 kt + 8 g .. +8 (zeros past the last query)
+  bf16x8_t qb[8];
+  const int qi = 32 * qblk + n32;
+  {
     const bf16_t* qp = q + (static_cast<size_t>(q0 + min(qi, nq - 1)) * H + h) * dq + 8 * g;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
       const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kt);
-      qb[nb][kt] = (qi < nq) ? v : bf16x8_t{};
+      qb[kt] = (qi < nq) ? v : bf16x8_t{};
     }
   }
 #pragma unroll
@@ -339,46 +342,52 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(const bf16_t* __rest
     *reinterpret_cast<uint4*>(ws + i * 256 + ((ch ^ am_swz(i)) * 16)) = wv[k];
   }
   __syncthreads();
-  // A operand of K-step kt for this wave's 32 columns: the lane mapping of the transposed
-  // read (4 rows x 4 columns per 16-lane group, two reads per operand)
+  // A operand of K-step kt for column block cb: the lane mapping of the transposed read (4
+  // rows x 4 columns per 16-lane group, two reads per operand); to[cb & 1][h4], and column
+  // blocks 2 and 3 are 128 bytes further on
   const int q16 = lane >> 4, L = lane & 15;
-  const int col = 32 * (wave & 1) + 16 * (q16 & 1) + 4 * (L & 3);
-  int to[2];
+  int to[2][2];
 #pragma unroll
-  for (int h4 = 0; h4 < 2; ++h4) {
-    const int i = 8 * (q16 >> 1) + 4 * h4 + (L >> 2);
-    to[h4] = i * 256 + (((col >> 3) ^ am_swz(i)) * 16) + (col & 7) * 2 + 128 * (wave >> 1);
-  }
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int h4 = 0; h4 < 2; ++h4) {
+      const int col = 32 * par + 16 * (q16 & 1) + 4 * (L & 3);
+      const int i = 8 * (q16 >> 1) + 4 * h4 + (L >> 2);
+      to[par][h4] = i * 256 + (((col >> 3) ^ am_swz(i)) * 16) + (col & 7) * 2;
+    }
   f32x16_t acc[NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16_t{};
+  for (int j = 0; j < NB; ++j) acc[j] = f32x16_t{};
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt) {
-    // rows 16 kt .. +16 keep the swizzle of rows 0 .. 15 (it reads row bits 1-3 only)
-    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4_t*)(const __attribute__((address_space(3))) char*)(ws + to[0] + 4096 * kt));
-    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4_t*)(const __attribute__((address_space(3))) char*)(ws + to[1] + 4096 * kt));
-    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[nb][kt], acc[nb], 0, 0, 0);
+    for (int j = 0; j < NB; ++j) {
+      const int cb = cb0 + j;
+      // rows 16 kt .. +16 keep the swizzle of rows 0 .. 15 (it reads row bits 1-3 only)
+      const int ofs = 4096 * kt + 128 * (cb >> 1);
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_t*)(const __attribute__((address_space(3))) char*)(ws + to[cb & 1][0] + ofs));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_t*)(const __attribute__((address_space(3))) char*)(ws + to[cb & 1][1] + ofs));
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[kt], acc[j], 0, 0, 0);
+    }
   }
-  // lane (query n32, half g) holds columns 8 (j / 4) + 4 g + j % 4 of the wave's 32
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int qi = 32 * nb + n32;
-    if (qi >= nq) continue;
+  // lane (query n32, half g) holds columns 8 (j / 4) + 4 g + j % 4 of each column block
+  if (qi < nq) {
     bf16_t* orow = q_abs + static_cast<size_t>(q0 + qi) * H * D + static_cast<size_t>(h) * D +
-                   c0 + 32 * wave + 4 * g;
+                   c0 + 4 * g;
 #pragma unroll
-    for (int jg = 0; jg < 4; ++jg) {
-      uint32_t pk[2];
+    for (int j = 0; j < NB; ++j) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
-        pk[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[nb][4 * jg + 2 * e]))) |
-                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[nb][4 * jg + 2 * e + 1]))) << 16);
-      *reinterpret_cast<uint2*>(orow + 8 * jg) = make_uint2(pk[0], pk[1]);
+      for (int jg = 0; jg < 4; ++jg) {
+        uint32_t pk[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          pk[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j][4 * jg + 2 * e]))) |
+                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j][4 * jg + 2 * e + 1]))) << 16);
+        *reinterpret_cast<uint2*>(orow + 32 * (cb0 + j) + 8 * jg) = make_uint2(pk[0], pk[1]);
+      }
     }
   }
   copy_rope_part(q, q_abs, q0, nq, H, h, d_n, d_r, d_c);
