@@ -5,9 +5,9 @@
 // summary": per-group K and V plus the shared RoPE key, from the same weights the
 // absorbed path uses).
 //
-// One workgroup (4 waves, one per SIMD) per (group j, range of pages).  The group's 256
+// One workgroup (8 waves, two per SIMD) per (group j, range of pages).  The group's 256
 // weight rows (W_UK[j] then W_UV[j], 512 wide) stay in registers for the whole range as the
-// A operand of v_mfma_f32_32x32x16_bf16 (64 rows per wave); pages stream through LDS in
+// A operand of v_mfma_f32_32x32x16_bf16 (32 rows per wave); pages stream through LDS in
 // halves of 32 tokens (Y^T[out][token] = W[out][:] . X^T[:][token], so both operands are read
 // along the latent, the layout they have in memory).  The latent rows go from global memory
 // straight into LDS (global_load_lds_dwordx4: no staging registers), two halves ahead,
@@ -17,6 +17,7 @@
 // Outputs are staged through LDS and written as whole 256-byte K and V rows at the start
 // of the next half, before its loads.  The G groups of a page range run on the same XCD
 // (workgroups 8 apart), so each page is fetched from HBM once and shared through its L2.
+
 #include <type_traits>
 
 #include "common.hpp"
@@ -37,7 +38,7 @@ constexpr int kYStride = 264;      // bf16 per staged output row (256 + 8: 16-by
 
 constexpr int kKrRowB = 128;       // RoPE-key bytes of one staged token (d_rope <= 64)
 constexpr int kXBuf = 3;           // half buffers in the latent ring
-constexpr int kBPF = 6;            // operand reads in flight ahead of their MFMAs
+constexpr int kBPF = 4;            // operand reads in flight ahead of their MFMAs
 
 struct ExpSmem {
   char x[kXBuf][kHalf * kXRowB];   // latent rows of three half pages (96 KB)
@@ -78,13 +79,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__global__ __launch_bounds__(256, 1) void expand_mfma_kernel(
+// With two waves per SIMD, a wave whose vector-memory instructions (4 latent rows and one
+// RoPE-key block loaded per half, 2 output stores) stall leaves the matrix core to the other
+// wave on its SIMD; the price is that every B operand read from LDS feeds one MFMA (32 rows)
+// instead of two (4.35 against 4.48-4.51 ms for one wave per SIMD with 64 rows each, at
+// 32 x 65536 tokens).  Waves 4-7 load the same RoPE-key blocks as waves 0-3 (the same bytes
+// to the same LDS addresses), so that every wave issues the same number of loads.
+__global__ __launch_bounds__(512, 1) void expand_mfma_kernel(
     const bf16_t* __restrict__ pool, const bf16_t* __restrict__ w_uk,
     const bf16_t* __restrict__ w_uv, bf16_t* __restrict__ kout, bf16_t* __restrict__ vout,
     bf16_t* __restrict__ krout, int num_pages, int G, int d_r, int n_ranges,
     int pages_per_range) {
   __shared__ __attribute__((aligned(16))) ExpSmem sm;
-  // workgroup -> (range r, group j): the G groups of one range are 8 workgroups apart
   const int wg = blockIdx.x;
   const int i8 = wg >> 3;
   const int j = i8 % G;
@@ -97,128 +103,125 @@ __global__ __launch_bounds__(256, 1) void expand_mfma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n32 = lane & 31, g = lane >> 5;
 
-  // weight rows 64 wave + 32 ob + n32 of the group's 256 (W_UK rows, then W_UV rows)
-  bf16x8 wreg[2][kLat / 16];
-#pragma unroll
-  for (int ob = 0; ob < 2; ++ob) {
-    const int o = 64 * wave + 32 * ob + n32;
+  // weight rows 32 wave + n32 of the group's 256 (W_UK rows, then W_UV rows)
+  bf16x8 wreg[kLat / 16];
+  {
+    const int o = 32 * wave + n32;
     const bf16_t* row = (o < kOut) ? w_uk + (static_cast<size_t>(j) * kOut + o) * kLat
                                    : w_uv + (static_cast<size_t>(j) * kOut + o - kOut) * kLat;
 #pragma unroll
     for (int ks = 0; ks < kLat / 16; ++ks)
-      wreg[ob][ks] = *reinterpret_cast<const bf16x8*>(row + 16 * ks + 8 * g);
+      wreg[ks] = *reinterpret_cast<const bf16x8*>(row + 16 * ks + 8 * g);
   }
   // Wait for the weight rows here, once (s_waitcnt vmcnt(0)).  Without it the compiler's
   // wait analysis, merging the loop's first entry (weights still in flight) with its back
   // edge, keeps a descending series of vmcnt waits on them inside the MFMA loop, and in
-  // every later half those waits force the next half's loads to land mid-loop, so loads
-  // and MFMAs ran one after the other.
+  // every later half those waits force the next half's loads to land mid-loop.
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  // each wave loads tokens 8 wave .. 8 wave + 7 of a half page, one 1-KB latent row per
-  // instruction (lane l brings 16-byte chunk l ^ (t & 15) of token t, so that LDS chunk l
-  // holds it where the swizzle puts it), and their RoPE keys in one more (lane l: token
-  // l / 8, 16-byte chunk l % 8; lanes past the key's width re-read its last chunk, and with
-  // no key the row's first).  All groups load the keys, so the count of loads in flight is
-  // the same in every workgroup; group 0 alone stores them.
+  // each wave loads the latent rows of tokens 4 wave .. 4 wave + 3 of a half page (one 1-KB
+  // row per instruction, lane l bringing 16-byte chunk l ^ (t & 15) of token t) and the RoPE
+  // keys of tokens 8 (wave % 4) .. +7 (lane l: token l / 8, chunk l % 8)
   const int n_half = 2 * (p1 - p0);
   const int per = d_r / 8;
-  const int kr_tok = lane >> 3;
+  const int kb = wave & 3;
+  const int kr_tok = 8 * kb + (lane >> 3);
   const int kr_ch = min(lane & 7, max(per - 1, 0));
   const int kr_ofs = per > 0 ? kLat + 8 * kr_ch : 0;
-  const bool kr_lane = j == 0 && (lane & 7) < per;
-  auto half_tok0 = [&](int h) {
-    return static_cast<size_t>(p0 + (h >> 1)) * 64 + 32 * (h & 1) + 8 * wave;
-  };
-  // load i (0..8) of half h into ring slot h % 3: i < 8 the latent row of token
-  // 8 wave + i, i = 8 the RoPE keys of the wave's 8 tokens.  Ordinary (cached) loads: the G
-  // workgroups of this range read the same rows, and all but the first must find them in L2.
+  const bool kr_lane = j == 0 && wave < 4 && (lane & 7) < per;
+  auto half_tok0 = [&](int h) { return static_cast<size_t>(p0 + (h >> 1)) * 64 + 32 * (h & 1); };
+  // load i (0..4) of half h into ring slot h % 3
+  // the per-lane parts of the addresses are formed at each use from an opaque copy of the
+  // lane index: kept live across the loop they would not leave the registers the weights need
   auto load_one = [&](int h, int i) {
     const int b = h % kXBuf;
     const char* rows = reinterpret_cast<const char*>(pool + half_tok0(h) * D);
-    if (i < 8) {
-      const int t = 8 * wave + i;
-      load_lds16(rows + i * 2 * D + 16 * (lane ^ (t & 15)), lds_addr(&sm.x[b][0]) + t * kXRowB);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    if (i < 4) {
+      const int t = 4 * wave + i;
+      load_lds16(rows + (t * 2 * D + 16 * (ln ^ (t & 15))), lds_addr(&sm.x[b][0]) + t * kXRowB);
     } else {
-      load_lds16(rows + 2 * (kr_tok * D + kr_ofs),
-                 lds_addr(&sm.kr[b][0]) + 8 * wave * kKrRowB);
+      const int kt = 8 * kb + (ln >> 3);
+      const int kc = min(ln & 7, max(per - 1, 0));
+      const int ko = per > 0 ? kLat + 8 * kc : 0;
+      load_lds16(rows + 2 * (kt * D + ko), lds_addr(&sm.kr[b][0]) + 8 * kb * kKrRowB);
     }
   };
-  // the outputs of half hprev (staged in ys = y[hprev & 1]) leave in four steps: 64 rows of
-  // 256 bytes (token t: its K row, then its V row), 16 lanes per row, one 16-byte store per
-  // lane and step; step it is 8 tokens further on (ostep elements)
-  const int o_t0 = threadIdx.x >> 5, o_kv = (threadIdx.x >> 4) & 1;
-  const int o_col = 8 * (threadIdx.x & 15);
-  const size_t ostep = static_cast<size_t>(8) * G * kOut;
-  auto read_outputs = [&](const bf16_t* ys, u32x4 (&val)[4]) {
-    const bf16_t* src = ys + o_t0 * kYStride + kOut * o_kv + o_col;
+  // outputs of half hprev leave in two steps: 32 rows of 256 bytes per step (token t: its K
+  // row, then its V row), 16 lanes per row, one 16-byte store per lane and step
+  const size_t ostep = static_cast<size_t>(16) * G * kOut;
+  auto read_outputs = [&](const bf16_t* ys, u32x4 (&val)[2]) {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    const bf16_t* src = ys + (t >> 5) * kYStride + kOut * ((t >> 4) & 1) + 8 * (t & 15);
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
-      val[it] = *reinterpret_cast<const u32x4*>(src + 8 * it * kYStride);
+    for (int it = 0; it < 2; ++it)
+      val[it] = *reinterpret_cast<const u32x4*>(src + 16 * it * kYStride);
   };
   auto output_dst = [&](int hprev) {
-    const size_t tok = static_cast<size_t>(p0 + (hprev >> 1)) * 64 + 32 * (hprev & 1) + o_t0;
-    return (o_kv ? vout : kout) + (tok * G + j) * kOut + o_col;
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    const size_t tok = half_tok0(hprev) + (t >> 5);
+    return (((t >> 4) & 1) ? vout : kout) + (tok * G + j) * kOut + 8 * (t & 15);
   };
-  // the end of half h: this wave's loads of half h + 1 have landed (the instructions issued
-  // after them, in order: the 4 output stores of half h - 1 when h > 0, group 0's key store,
-  // the 9 loads of half h + 2 when there is one; the key store is left out of the count,
-  // which only makes the wait cover it too), its output staging too; then the barrier.
-  // The counts assume no vector-memory instructions of the compiler's own in the loop: the
-  // kernel uses no scratch (a spill's scratch accesses would count here too).
+  // the end of half h: this wave's loads of half h + 1 have landed (issued after them: the 2
+  // output stores of half h - 1 when h > 0, group 0's key store, the 5 loads of half h + 2
+  // when there is one; the key store is left out of the count, which only makes the wait
+  // cover it too), its output staging too; then the barrier.  The kernel uses no scratch.
   auto end_half = [&](int h) {
     if (h + 1 >= n_half)
       wait_vm_lgkm0<63>();
     else if (h + 2 < n_half)
-      h > 0 ? wait_vm_lgkm0<13>() : wait_vm_lgkm0<9>();
+      h > 0 ? wait_vm_lgkm0<7>() : wait_vm_lgkm0<5>();
     else
-      h > 0 ? wait_vm_lgkm0<4>() : wait_vm_lgkm0<0>();
+      h > 0 ? wait_vm_lgkm0<2>() : wait_vm_lgkm0<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // every workgroup here has n_half >= 2: its two first halves go out now
 #pragma unroll
-  for (int i = 0; i < 9; ++i) load_one(0, i);
+  for (int i = 0; i < 5; ++i) load_one(0, i);
 #pragma unroll
-  for (int i = 0; i < 9; ++i) load_one(1, i);
-  wait_vm_lgkm0<9>();
+  for (int i = 0; i < 5; ++i) load_one(1, i);
+  wait_vm_lgkm0<5>();
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  // one half page; P = h & 1 as a constant, so the staging buffer's address is fixed
   auto half = [&](auto par, int h) {
     constexpr int P = decltype(par)::value;
     const int b = h % kXBuf;
-    // half h has landed in ring slot b; the outputs of half h - 1 are staged in y[1 - P];
-    // the ring slot and staging buffer refilled below were last read before this barrier.
-    // The half's vector-memory instructions go out here, before the MFMA loop (the 4 output
-    // stores of half h - 1, group 0's key store, the 9 loads of half h + 2, in that order).
-    // Spread over the loop instead (one every other K-step), they lengthened the loop by
-    // what they saved here: the CU's vector-memory path is what they wait for.
     if (h > 0) {
-      u32x4 oval[4];
+      u32x4 oval[2];
       read_outputs(sm.y[1 - P], oval);
       bf16_t* odst = output_dst(h - 1);
 #pragma unroll
-      for (int it = 0; it < 4; ++it)
+      for (int it = 0; it < 2; ++it)
         __builtin_nontemporal_store(oval[it], reinterpret_cast<u32x4*>(odst + it * ostep));
     }
-    if (kr_lane) {   // the shared RoPE key, copied once per token (group 0)
-      const u32x4 key = *reinterpret_cast<const u32x4*>(&sm.kr[b][0] + 8 * wave * kKrRowB +
+    if (kr_lane) {
+      const u32x4 key = *reinterpret_cast<const u32x4*>(&sm.kr[b][0] + 8 * kb * kKrRowB +
                                                         16 * lane);
       __builtin_nontemporal_store(
           key, reinterpret_cast<u32x4*>(krout + (half_tok0(h) + kr_tok) * d_r + 8 * kr_ch));
     }
     if (h + 2 < n_half) {
 #pragma unroll
-      for (int i = 0; i < 9; ++i) load_one(h + 2, i);
+      for (int i = 0; i < 5; ++i) load_one(h + 2, i);
     }
-    f32x16 acc[2] = {};
-    const char* bt = &sm.x[b][0] + n32 * kXRowB;
+    f32x16 acc = {};
+    // chunk 2 ks + g of token n32 sits at (2 ks + g) ^ (n32 & 15): 8 per-lane offsets for
+    // ks % 8, the rest (256 bytes per 8 K-steps) an immediate
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int tn = ln & 31, tg = ln >> 5;
+    const char* bt = &sm.x[b][0] + tn * kXRowB;
+    int bo[8];
+#pragma unroll
+    for (int k8 = 0; k8 < 8; ++k8) bo[k8] = 16 * ((2 * k8 + tg) ^ (tn & 15));
     auto read_b = [&](int ks) {
-      return *reinterpret_cast<const bf16x8*>(bt + 16 * xswz(n32, 2 * ks + g));
+      return *reinterpret_cast<const bf16x8*>(bt + bo[ks & 7] + 256 * (ks >> 3));
     };
     bf16x8 bbuf[kBPF];
 #pragma unroll
@@ -226,22 +229,17 @@ __global__ __launch_bounds__(256, 1) void expand_mfma_kernel(
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < kLat / 16; ++ks) {
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wreg[0][ks], bbuf[ks % kBPF], acc[0],
-                                                       0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wreg[1][ks], bbuf[ks % kBPF], acc[1],
-                                                       0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wreg[ks], bbuf[ks % kBPF], acc, 0, 0, 0);
       if (ks + kBPF < kLat / 16) bbuf[ks % kBPF] = read_b(ks + kBPF);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // lane (n32, g) holds token n32, outputs 32 ob + 8 q + 4 g + 0..3 of the wave's 64
-    bf16_t* yrow = sm.y[P] + n32 * kYStride + 64 * wave + 4 * g;
+    // lane (n32, g) holds token n32, outputs 8 q + 4 g + 0..3 of the wave's 32
+    bf16_t* yrow = sm.y[P] + n32 * kYStride + 32 * wave + 4 * g;
 #pragma unroll
-    for (int ob = 0; ob < 2; ++ob)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<uint2*>(yrow + 32 * ob + 8 * q) =
-            make_uint2(pack_bf16x2(acc[ob][4 * q], acc[ob][4 * q + 1]),
-                       pack_bf16x2(acc[ob][4 * q + 2], acc[ob][4 * q + 3]));
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint2*>(yrow + 8 * q) =
+          make_uint2(pack_bf16x2(acc[4 * q], acc[4 * q + 1]),
+                     pack_bf16x2(acc[4 * q + 2], acc[4 * q + 3]));
     end_half(h);
   };
   for (int h = 0;; h += 2) {   // n_half is even
@@ -249,13 +247,12 @@ __global__ __launch_bounds__(256, 1) void expand_mfma_kernel(
     half(std::integral_constant<int, 1>(), h + 1);
     if (h + 2 >= n_half) break;
   }
-  // the last half's outputs
   {
-    u32x4 oval[4];
+    u32x4 oval[2];
     read_outputs(sm.y[(n_half - 1) & 1], oval);
     bf16_t* odst = output_dst(n_half - 1);
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+    for (int it = 0; it < 2; ++it)
       __builtin_nontemporal_store(oval[it], reinterpret_cast<u32x4*>(odst + it * ostep));
   }
 }
@@ -274,7 +271,7 @@ hipError_t launch_expand_cache_mfma(const mla_shape_t& s, const void* pool, cons
   // page ranges: a multiple of 8 (one per XCD slot), about 256 workgroups in all
   const int n_ranges = max(8, (256 / G) / 8 * 8);
   const int per = (s.num_pages + n_ranges - 1) / n_ranges;
-  hipLaunchKernelGGL(expand_mfma_kernel, dim3(n_ranges * G), dim3(256), 0, st,
+  hipLaunchKernelGGL(expand_mfma_kernel, dim3(n_ranges * G), dim3(512), 0, st,
                      static_cast<const bf16_t*>(pool), static_cast<const bf16_t*>(w_uk),
                      static_cast<const bf16_t*>(w_uv), static_cast<bf16_t*>(k),
                      static_cast<bf16_t*>(v), static_cast<bf16_t*>(kr), s.num_pages, G,
