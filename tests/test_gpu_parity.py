@@ -149,6 +149,7 @@ def test_tiny_f32_step_entry_point_matches_steps():
     ("dsv2-b16-t4096", 1, [4096, 577, 64, 33], 32),
     ("dsv2-b16-t4096", 2, [1 + (97 * i) % 300 for i in range(20)], 3),
     ("dsv2-b16-t4096", 2, [2 + (53 * i) % 400 for i in range(33)], 4),
+    ("dsv2-b16-t4096", 2, [1280 + 37 * i for i in range(33)], 20),
     ("dsv2-b16-t4096", 1, [5000, 64], 64),
     ("dsv2-b16-t4096", 2, [1, 2, 130], 1),
     ("dsv2-b16-t4096", 1, [0, 577, 0, 64], 4),
@@ -160,8 +161,9 @@ def test_bf16_step_entry_point_matches_steps(name, s_q, ctx, S):
     """At bf16 with d_c 512 and d_v 128 the step entry point merges the splits and
     up-projects in one kernel; its outputs must equal those of the separate entry points
     bit for bit (20 and 33 sequences at s_q = 2 give two and three query blocks of 32, the
-    last ragged, on the fused kernel with whole heads per workgroup, 4 queries on the one
-    with half heads;
+    last ragged, on the fused kernel with whole heads per workgroup, which loads the
+    partials 8 splits at a time, so 20 splits take three batches; 4 queries on the one with
+    half heads;
     s_q = 2 over one token gives rows with no visible token, and sequences of length 0 give
     whole sequences of empty chunks; the 32- and 4-head shapes have too few workgroups for
     the fused kernel and take the separate kernels inside the step), and match the oracle."""
