@@ -67,10 +67,9 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
 }
 
-// The 16-byte chunk ch of staged token t sits at chunk ch ^ (t & 15) of its row: the
-// operand reads take one chunk from each of 16 consecutive tokens (conflict-free), the
-// staging stores write whole rows.
-__device__ __forceinline__ int xswz(int t, int ch) { return ch ^ (t & 15); }
+// Ring layout: the 16-byte chunk ch of staged token t sits at chunk ch ^ (t & 15) of its
+// row, so the operand reads, one chunk from each of 16 consecutive tokens, are
+// conflict-free, and each load instruction still writes one whole row.
 
 // two floats to a pair of bf16, rounded to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
