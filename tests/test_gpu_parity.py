@@ -150,6 +150,7 @@ def test_tiny_f32_step_entry_point_matches_steps():
     ("dsv2-b16-t4096", 2, [1 + (97 * i) % 300 for i in range(20)], 3),
     ("dsv2-b16-t4096", 2, [2 + (53 * i) % 400 for i in range(33)], 4),
     ("dsv2-b16-t4096", 2, [1280 + 37 * i for i in range(33)], 20),
+    ("dsv2-b16-t4096", 2, [0 if i % 5 == 0 else 1 + (71 * i) % 500 for i in range(33)], 6),
     ("dsv2-b16-t4096", 1, [4096 - 61 * i for i in range(16)], 8),
     ("dsv2-b16-t4096", 1, [300 + 29 * i for i in range(32)], 6),
     ("dsv2-b16-t4096", 1, [5000, 64], 64),
@@ -164,7 +165,8 @@ def test_bf16_step_entry_point_matches_steps(name, s_q, ctx, S):
     up-projects in one kernel; its outputs must equal those of the separate entry points
     bit for bit (20 and 33 sequences at s_q = 2 give two and three query blocks of 32, the
     last ragged, on the fused kernel with whole heads per workgroup, which loads the
-    partials 8 splits at a time, so 20 splits take three batches; 4, 16 and 32 queries on the
+    partials 8 splits at a time, so 20 splits take three batches, and empty sequences
+    among them give rows whose chunks are all empty; 4, 16 and 32 queries on the
     one with half heads, which merges four queries a pass);
     s_q = 2 over one token gives rows with no visible token, and sequences of length 0 give
     whole sequences of empty chunks; the 32- and 4-head shapes have too few workgroups for
