@@ -419,6 +419,51 @@ __device__ __forceinline__ void rescale_if_moved(Smem& sm, int k, int n32,
 // Value wave VW of the 32-row layout: latent columns [256 VW, 256 VW + 256) of the block's
 // rows (32 NQ).  It also streams half of every tile through the ring (below) and, in slot s,
 // multiplies tile s-2.
+// A value wave's epilogue: its 32 NQ rows x 32 KMB latent columns of O^T, each row scaled
+// by 1 / (its softmax sum), go to o_part.  In the MFMA layout a store instruction would
+// write 32-byte pieces of 32 rows; the ring is free once every wave has passed the last
+// barrier, so the block is staged there row-major (each of at most NVW value waves in its
+// own part) and leaves in whole 1-KB row segments, which shortens the burst of partial
+// writes that ends the kernel.  Same products as a direct store, so the same bits.
+template <int NQ, int KMB, int NVW>
+__device__ __forceinline__ void write_partials(Smem& sm, const Work& w, int vw, int lat0,
+                                               const f32x16 (&acc)[KMB][NQ], int lane) {
+  constexpr int kCols = 32 * KMB, kRows = 32 * NQ;
+  constexpr int kStg = kCols + 4;          // floats per staged row (padded)
+  constexpr int kPerRow = kCols / 4;       // float4 per row
+  static_assert(NVW * kRows * kStg * 4 <= static_cast<int>(sizeof(sm.ring)),
+                "staged partials exceed the ring");
+  static_assert(64 % kPerRow == 0 || kPerRow % 64 == 0, "row segments and the wave");
+  const int n32 = lane & 31, g = lane >> 5;
+  float* stg = reinterpret_cast<float*>(&sm.ring[0][0]) + vw * kRows * kStg;
+#pragma unroll
+  for (int nb = 0; nb < NQ; ++nb) {
+    const float l = sm.lfin[32 * nb + n32];
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    float* srow = stg + (32 * nb + n32) * kStg + 4 * g;
+#pragma unroll
+    for (int mb = 0; mb < KMB; ++mb)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float4 v;
+        v.x = acc[mb][nb][4 * a + 0] * inv;
+        v.y = acc[mb][nb][4 * a + 1] * inv;
+        v.z = acc[mb][nb][4 * a + 2] * inv;
+        v.w = acc[mb][nb][4 * a + 3] * inv;
+        *reinterpret_cast<float4*>(srow + 32 * mb + 8 * a) = v;
+      }
+  }
+  // read back by this wave only (its LDS operations complete in order): instruction i
+  // covers 256 consecutive floats of the block, row r = idx / kPerRow
+  float* obase = w.o_part + (w.qrow0 * w.S + w.u) * kDC + lat0;
+#pragma unroll 8
+  for (int i = 0; i < kRows * kPerRow / 64; ++i) {
+    const int idx = 64 * i + lane, r = idx / kPerRow, c4 = 4 * (idx - r * kPerRow);
+    const float4 v = *reinterpret_cast<const float4*>(stg + r * kStg + c4);
+    *reinterpret_cast<float4*>(obase + static_cast<size_t>(r) * w.S * kDC + c4) = v;
+  }
+}
+
 template <int NQ, int VW>
 __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
   const int n32 = lane & 31, g = lane >> 5;
@@ -506,25 +551,7 @@ __device__ __forceinline__ void value_wave(Smem& sm, const Work& w, int lane) {
       }
     }
     __syncthreads();   // the score waves have published the row sums
-#pragma unroll
-    for (int nb = 0; nb < NQ; ++nb) {
-      const float l = sm.lfin[32 * nb + n32];
-      const float inv = (l > 0.f) ? 1.f / l : 0.f;
-      float* orow = w.o_part + ((w.qrow0 + 32 * nb + n32) * w.S + w.u) * kDC + lat0 + 4 * g;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          // a few accumulators at a time, so the epilogue needs only a few VGPRs
-          __builtin_amdgcn_sched_barrier(0);
-          float4 v;
-          v.x = acc[mb][nb][4 * a + 0] * inv;
-          v.y = acc[mb][nb][4 * a + 1] * inv;
-          v.z = acc[mb][nb][4 * a + 2] * inv;
-          v.w = acc[mb][nb][4 * a + 3] * inv;
-          *reinterpret_cast<float4*>(orow + 32 * mb + 8 * a) = v;
-        }
-    }
+    write_partials<NQ, 8, 2>(sm, w, VW, lat0, acc, lane);
     return;
   }
 }
@@ -638,24 +665,7 @@ __device__ __forceinline__ void value_wave128(Smem& sm, const Work& w, int lane)
       }
     }
     __syncthreads();
-#pragma unroll
-    for (int nb = 0; nb < NQ; ++nb) {
-      const float l = sm.lfin[32 * nb + n32];
-      const float inv = (l > 0.f) ? 1.f / l : 0.f;
-      float* orow = w.o_part + ((w.qrow0 + 32 * nb + n32) * w.S + w.u) * kDC + lat0 + 4 * g;
-#pragma unroll
-      for (int mb = 0; mb < KMB; ++mb)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          __builtin_amdgcn_sched_barrier(0);
-          float4 v;
-          v.x = acc[mb][nb][4 * a + 0] * inv;
-          v.y = acc[mb][nb][4 * a + 1] * inv;
-          v.z = acc[mb][nb][4 * a + 2] * inv;
-          v.w = acc[mb][nb][4 * a + 3] * inv;
-          *reinterpret_cast<float4*>(orow + 32 * mb + 8 * a) = v;
-        }
-    }
+    write_partials<NQ, KMB, 4>(sm, w, VW, lat0, acc, lane);
     return;
   }
 }
