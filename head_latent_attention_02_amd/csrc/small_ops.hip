@@ -373,21 +373,45 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(const bf16_t* __rest
       acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[kt], acc[j], 0, 0, 0);
     }
   }
-  // lane (query n32, half g) holds columns 8 (j / 4) + 4 g + j % 4 of each column block
-  if (qi < nq) {
-    bf16_t* orow = q_abs + static_cast<size_t>(q0 + qi) * H * D + static_cast<size_t>(h) * D +
-                   c0 + 4 * g;
+  // lane (query n32, half g) holds columns 8 (j / 4) + 4 g + j % 4 of each column block.
+  // Stored as they are, each store instruction writes 16-byte pieces of 32 query rows.  With
+  // two or more query blocks (over 32 queries) the outputs are first staged in ws (free once every wave
+  // has read its last operands; rows of 256 bytes, 16-byte chunks XOR-swizzled by row) and
+  // leave as whole 256-byte rows, four per store instruction: a1 at 128 queries 21.5 ->
+  // 17.5 us.  For one query block (16 queries) staging measured no gain, so that case keeps
+  // the direct stores and their one barrier fewer.
+  auto pack = [&](int j, int jg, int e) {
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j][4 * jg + 2 * e]))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j][4 * jg + 2 * e + 1]))) << 16);
+  };
+  if constexpr (NB == 1) {
+    if (qi < nq) {
+      bf16_t* orow = q_abs + static_cast<size_t>(q0 + qi) * H * D + static_cast<size_t>(h) * D +
+                     c0 + 4 * g;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
+      for (int jg = 0; jg < 4; ++jg)
+        *reinterpret_cast<uint2*>(orow + 32 * cb0 + 8 * jg) = make_uint2(pack(0, jg, 0), pack(0, jg, 1));
+    }
+  } else {
+    __syncthreads();
+    char* srow = ws + (32 * qblk + n32) * 256;
+    const int sw = n32 & 15;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
-        uint32_t pk[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          pk[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j][4 * jg + 2 * e]))) |
-                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j][4 * jg + 2 * e + 1]))) << 16);
-        *reinterpret_cast<uint2*>(orow + 32 * (cb0 + j) + 8 * jg) = make_uint2(pk[0], pk[1]);
+        const int ch = 4 * (cb0 + j) + jg;   // 16-byte chunk of the 256-byte row
+        *reinterpret_cast<uint2*>(srow + ((ch ^ sw) * 16) + 8 * g) =
+            make_uint2(pack(j, jg, 0), pack(j, jg, 1));
       }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2 * NB; ++k) {
+      const int idx = tid + 256 * k, r = idx >> 4, ch = idx & 15;
+      if (r < nq)
+        *reinterpret_cast<uint4*>(q_abs + static_cast<size_t>(q0 + r) * H * D +
+                                  static_cast<size_t>(h) * D + c0 + 8 * ch) =
+            *reinterpret_cast<const uint4*>(ws + r * 256 + ((ch ^ (r & 15)) * 16));
     }
   }
   copy_rope_part(q, q_abs, q0, nq, H, h, d_n, d_r, d_c);
@@ -762,16 +786,40 @@ __global__ __launch_bounds__(256 * NV) void combine_out_uv_kernel(
   }
   __syncthreads();
   // lane (query m, half g) holds value rows 8 (j / 4) + 4 g + j % 4 of block vb; the
-  // quarters are summed in order 0, 1, 2, 3
-  if (kq == 0 && m < nqb) {
-    float* orow = out + (static_cast<size_t>(q0 + m) * H + h) * d_v + v0;
+  // quarters are summed in order 0, 1, 2, 3.  Stored as they are, each store instruction
+  // writes 4-byte pieces of 32 query rows.  With whole heads (NV = 4) the sums are staged in
+  // ob (free after the up-projection's operand reads, which the barrier above ends) as
+  // [query][128 value rows] fp32 and leave as whole 512-byte rows (the ragged MTP step
+  // ~2 us faster); with half heads the direct stores measured as fast.
+  auto quarter_sum = [&](int j) {
+    float t = acc2[j];
+    t += red[vb][0][j][lane];
+    t += red[vb][1][j][lane];
+    t += red[vb][2][j][lane];
+    return t;
+  };
+  if constexpr (NV == 2) {
+    if (kq == 0 && m < nqb) {
+      float* orow = out + (static_cast<size_t>(q0 + m) * H + h) * d_v + v0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      float t = acc2[j];
-      t += red[vb][0][j][lane];
-      t += red[vb][1][j][lane];
-      t += red[vb][2][j][lane];
-      orow[8 * (j >> 2) + 4 * g + (j & 3)] = t;
+      for (int j = 0; j < 16; ++j) orow[8 * (j >> 2) + 4 * g + (j & 3)] = quarter_sum(j);
+    }
+  } else {
+    constexpr int kOutRow = 32 * NV + 4;   // floats per staged row (padded)
+    static_assert(kFuQ * kOutRow * 4 <= static_cast<int>(sizeof(ob)), "staged outputs exceed ob");
+    float* ost = reinterpret_cast<float*>(ob);
+    if (kq == 0) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        ost[m * kOutRow + 32 * vb + 8 * (j >> 2) + 4 * g + (j & 3)] = quarter_sum(j);
+    }
+    __syncthreads();
+    constexpr int kPerRow = 8 * NV;   // float4 per row
+    for (int idx = tid; idx < nqb * kPerRow; idx += 256 * NV) {
+      const int r = idx / kPerRow, c4 = 4 * (idx - r * kPerRow);
+      *reinterpret_cast<float4*>(out + (static_cast<size_t>(q0 + r) * H + h) * d_v +
+                                 32 * NV * half + c4) =
+          *reinterpret_cast<const float4*>(ost + r * kOutRow + c4);
     }
   }
 }
