@@ -188,7 +188,15 @@ __global__ __launch_bounds__(512, 1) void expand_mfma_kernel(
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  auto half = [&](auto par, int h) {
+  // The vector-memory work of half h: the outputs of half h - 1 (staged in LDS before the
+  // last barrier), group 0's RoPE keys of half h, the loads of half h + 2 into the ring slot
+  // that half h - 1 used.  Waves 0-3 issue it when the half starts; waves 4-7, which share
+  // SIMDs with them, half-way through their MFMA loop, so that on each SIMD one wave's memory
+  // issue overlaps the other's matrix work (issued together, every wave's issue stalled on
+  // the CU's vector-memory path while the matrix cores idled).  Either way it is issued
+  // before the half's end, so end_half's counts hold for both.
+  const bool late = wave >= 4;
+  auto issue = [&](auto par, int h) {
     constexpr int P = decltype(par)::value;
     const int b = h % kXBuf;
     if (h > 0) {
@@ -209,6 +217,11 @@ __global__ __launch_bounds__(512, 1) void expand_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 5; ++i) load_one(h + 2, i);
     }
+  };
+  auto half = [&](auto par, int h) {
+    constexpr int P = decltype(par)::value;
+    const int b = h % kXBuf;
+    if (!late) issue(par, h);
     f32x16 acc = {};
     // chunk 2 ks + g of token n32 sits at (2 ks + g) ^ (n32 & 15): 8 per-lane offsets for
     // ks % 8, the rest (256 bytes per 8 K-steps) an immediate
@@ -231,6 +244,10 @@ __global__ __launch_bounds__(512, 1) void expand_mfma_kernel(
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wreg[ks], bbuf[ks % kBPF], acc, 0, 0, 0);
       if (ks + kBPF < kLat / 16) bbuf[ks % kBPF] = read_b(ks + kBPF);
       __builtin_amdgcn_sched_barrier(0);
+      if (ks == kLat / 32 - 1) {
+        if (late) issue(par, h);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // lane (n32, g) holds token n32, outputs 8 q + 4 g + 0..3 of the wave's 32
     bf16_t* yrow = sm.y[P] + n32 * kYStride + 32 * wave + 4 * g;
