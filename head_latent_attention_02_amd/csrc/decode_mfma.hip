@@ -673,8 +673,13 @@ __device__ __forceinline__ void value_wave128(Smem& sm, const Work& w, int lane)
 }  // namespace ring
 
 // Workgroup -> (sequence, chunk, row block): the row blocks of one (b, u) are 8 workgroups
-// apart, so they run on the same XCD; the grid's padding workgroups return (uniform for the
-// whole workgroup, before any barrier).  Expanded inside each kernel: filled through a
+// apart, so they run on the same XCD.  When the grid runs in one round (a CU per
+// workgroup), XCD x (workgroup % 8) takes the x-th contiguous range of the (b, u) units, so
+// that an XCD holds the chunks of few sequences and its L2 fetches only their q_abs rows
+// (decode at 16 x 4096 tokens ~0.7 us, at 4 x 131072 ~1 us faster); in longer grids consecutive units go to consecutive XCDs,
+// which spreads every sequence over all XCDs and keeps their queues balanced when lengths
+// differ (contiguous ranges made the ragged MTP decode 627 -> 769 us).  The grid's padding
+// workgroups return (uniform for the whole workgroup, before any barrier).  Expanded inside each kernel: filled through a
 // helper, the page-table reads lose their scalar (s_load) form, and a vector read of a page
 // entry waits, through the in-order load counter, for every tile load in flight.
 #define MLA_SETUP_WORK(NQ)                                                           \
@@ -683,7 +688,8 @@ __device__ __forceinline__ void value_wave128(Smem& sm, const Work& w, int lane)
     const int wg = blockIdx.x;                                                     \
     const int rest = wg >> 3;                                                      \
     const int y = rest % n_yblk;                                                   \
-    const int unit = (rest / n_yblk) * 8 + (wg & 7);                               \
+    const int unit = xcd_ranges ? (wg & 7) * ((n_units + 7) >> 3) + rest / n_yblk   \
+                                : (rest / n_yblk) * 8 + (wg & 7);                  \
     if (unit >= n_units) return;                                                   \
     const int b = unit / S;                                                        \
     w.u = unit - b * S;                                                            \
@@ -715,7 +721,7 @@ void decode_absorbed_mfma_r32_kernel(
     const int32_t* __restrict__ pt, const int32_t* __restrict__ lens,
     float* __restrict__ o_part, float* __restrict__ lse_part, int s_q, int H, int max_pages,
     int S, int split_tokens, float zscale, float slack, int n_units, int n_yblk,
-    int num_pages, unsigned int* bad) {
+    int xcd_ranges, int num_pages, unsigned int* bad) {
   constexpr int NQ = 1;
   __shared__ __attribute__((aligned(16))) ring::Smem sm;
   MLA_SETUP_WORK(NQ)
@@ -739,7 +745,7 @@ __global__ __launch_bounds__(512, 1) void decode_absorbed_mfma_r64_kernel(
     const int32_t* __restrict__ pt, const int32_t* __restrict__ lens,
     float* __restrict__ o_part, float* __restrict__ lse_part, int s_q, int H, int max_pages,
     int S, int split_tokens, float zscale, float slack, int n_units, int n_yblk,
-    int num_pages, unsigned int* bad) {
+    int xcd_ranges, int num_pages, unsigned int* bad) {
   constexpr int NQ = 2;
   __shared__ __attribute__((aligned(16))) ring::Smem sm;
   MLA_SETUP_WORK(NQ)
@@ -775,6 +781,8 @@ hipError_t launch_decode_absorbed_mfma(const mla_shape_t& s, const void* q_abs,
   const int n_yblk = rows / (32 * nq);
   const int n_units = s.batch * s.n_splits;
   const unsigned grid = static_cast<unsigned>((n_units + 7) / 8) * 8u * n_yblk;
+  constexpr unsigned kOneRound = 256;   // workgroups that run at once: one per CU
+  const int xcd_ranges = grid <= kOneRound ? 1 : 0;
   const float zscale = s.softmax_scale * kLog2e;
   // Slack (log2 units) before a row's reference maximum moves; the default keeps P below
   // 2^32.  MLA_DECODE_REF_SLACK (0..64) overrides it, e.g. 0 to exercise the rescale path.
@@ -787,12 +795,14 @@ hipError_t launch_decode_absorbed_mfma(const mla_shape_t& s, const void* q_abs,
     hipLaunchKernelGGL(decode_absorbed_mfma_r64_kernel, dim3(grid), dim3(512), 0, st,
                        static_cast<const bf16_t*>(q_abs), static_cast<const bf16_t*>(pool), pt,
                        lens, o_part, lse_part, s.s_q, s.n_heads, s.max_pages, s.n_splits,
-                       s.split_tokens, zscale, slack, n_units, n_yblk, s.num_pages, bad);
+                       s.split_tokens, zscale, slack, n_units, n_yblk, xcd_ranges,
+                       s.num_pages, bad);
   else
     hipLaunchKernelGGL(decode_absorbed_mfma_r32_kernel, dim3(grid), dim3(192), 0, st,
                        static_cast<const bf16_t*>(q_abs), static_cast<const bf16_t*>(pool), pt,
                        lens, o_part, lse_part, s.s_q, s.n_heads, s.max_pages, s.n_splits,
-                       s.split_tokens, zscale, slack, n_units, n_yblk, s.num_pages, bad);
+                       s.split_tokens, zscale, slack, n_units, n_yblk, xcd_ranges,
+                       s.num_pages, bad);
   return hipGetLastError();
 }
 
