@@ -673,15 +673,16 @@ __device__ __forceinline__ void value_wave128(Smem& sm, const Work& w, int lane)
 }  // namespace ring
 
 // Workgroup -> (sequence, chunk, row block): the row blocks of one (b, u) are 8 workgroups
-// apart, so they run on the same XCD.  When the grid runs in one round (a CU per
-// workgroup), XCD x (workgroup % 8) takes the x-th contiguous range of the (b, u) units, so
-// that an XCD holds the chunks of few sequences and its L2 fetches only their q_abs rows
-// (decode at 16 x 4096 tokens ~0.7 us, at 4 x 131072 ~1 us faster); in longer grids consecutive units go to consecutive XCDs,
-// which spreads every sequence over all XCDs and keeps their queues balanced when lengths
-// differ (contiguous ranges made the ragged MTP decode 627 -> 769 us).  The grid's padding
-// workgroups return (uniform for the whole workgroup, before any barrier).  Expanded inside each kernel: filled through a
-// helper, the page-table reads lose their scalar (s_load) form, and a vector read of a page
-// entry waits, through the in-order load counter, for every tile load in flight.
+// apart, so they run on the same XCD.  When every workgroup of the grid has a CU at once,
+// XCD x (workgroup % 8) takes the x-th contiguous range of the (b, u) units, so that an XCD
+// holds the chunks of few sequences and its L2 fetches only their q_abs rows (decode at
+// 16 x 4096 tokens ~0.7 us, at 4 x 131072 ~1 us faster).  In longer grids consecutive units
+// go to consecutive XCDs, which spreads every sequence over all XCDs and keeps their queues
+// balanced when lengths differ (contiguous ranges made the ragged MTP decode 627 -> 769 us).
+// The grid's padding workgroups return (uniform for the whole workgroup, before any
+// barrier).  Expanded inside each kernel: filled through a helper, the page-table reads lose
+// their scalar (s_load) form, and a vector read of a page entry waits, through the in-order
+// load counter, for every tile load in flight.
 #define MLA_SETUP_WORK(NQ)                                                           \
   Work w;                                                                          \
   {                                                                                \
@@ -781,8 +782,8 @@ hipError_t launch_decode_absorbed_mfma(const mla_shape_t& s, const void* q_abs,
   const int n_yblk = rows / (32 * nq);
   const int n_units = s.batch * s.n_splits;
   const unsigned grid = static_cast<unsigned>((n_units + 7) / 8) * 8u * n_yblk;
-  constexpr unsigned kOneRound = 256;   // workgroups that run at once: one per CU
-  const int xcd_ranges = grid <= kOneRound ? 1 : 0;
+  constexpr unsigned kResident = 256;   // workgroups resident at once: one per CU
+  const int xcd_ranges = grid <= kResident ? 1 : 0;
   const float zscale = s.softmax_scale * kLog2e;
   // Slack (log2 units) before a row's reference maximum moves; the default keeps P below
   // 2^32.  MLA_DECODE_REF_SLACK (0..64) overrides it, e.g. 0 to exercise the rescale path.
